@@ -1,0 +1,147 @@
+/*
+ * kpool.h - C ABI of the MI355X (gfx950) k-pool DSA indexer selection.
+ *
+ * The selection a DSA indexer makes for each query row (pages: Atlas
+ * inference docs, spark_model/layers/glm5next_dsa/tp.rs, module doc "Why the
+ * indexer is REPLICATED, not sharded"; Megatron-LM PR #8299, sections
+ * "Mechanism" and "Change"):
+ *
+ *   1. pool the keys over kpool consecutive tokens            kpool_pool_keys
+ *   2. score every causally visible pool of row i as
+ *        S[i,p] = sum_h w[i,h] * relu(scale * <q[i,h,:], kp[p,:]>)
+ *      and keep the best `budget` pools, higher score first and the
+ *      smaller pool index on equal scores                     kpool_score_topk
+ *   3. expand the kept pools to token ids p*kpool + j and drop the tokens
+ *      that come after the row                                kpool_expand
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory, keeps no pointer after it returns and never
+ *     synchronises: all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream).  Results are ready when the stream reaches them.
+ *   - bf16 tensors are passed as their uint16_t bit patterns.  Tensors are
+ *     row-major and contiguous; q, kp, k and w must be 16-byte aligned.
+ *   - Packed variable-length batches ("THD") are described by cu_seqlens:
+ *     sequence s holds the global rows [cu_seqlens[s], cu_seqlens[s+1]).
+ *     Positions, pool ids and token ids are SEQUENCE-LOCAL: row i of
+ *     sequence s sits at t = i - cu_seqlens[s], and sees the pools p with
+ *     p*kpool <= t.  A single sequence is nseq = 1, cu_seqlens = {0, T}.
+ *     `cu_seqlens_host` is a host copy used to validate and plan launches;
+ *     `cu_seqlens_dev` / `cu_pools_dev` hold the same arrays on the device.
+ *   - Every entry point validates its arguments before it launches anything
+ *     and returns KPOOL_OK (0) or a negative kpool_status; the reason is then
+ *     in kpool_last_error() (thread-local).  Nothing is thrown across the ABI.
+ *     Launch failures map to KPOOL_EHIP; faults that happen while a kernel
+ *     runs surface at the caller's next synchronisation.
+ *   - Calls on one stream are ordered; the library holds no global state
+ *     except the optional profiler below, so concurrent calls on different
+ *     streams are independent.
+ */
+#ifndef KPOOL_H
+#define KPOOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KPOOL_OK = 0,
+  KPOOL_EINVAL = -1,       /* bad argument: range, size, pointer, alignment */
+  KPOOL_EUNSUPPORTED = -2, /* head count / head dim not compiled in */
+  KPOOL_EWORKSPACE = -3,   /* workspace smaller than one score row */
+  KPOOL_EHIP = -4          /* a HIP launch or runtime call failed */
+} kpool_status;
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char *kpool_last_error(void);
+
+/* ABI version (major*100 + minor). */
+int kpool_version(void);
+
+/* Pool bookkeeping on the host (Atlas tp.rs module doc: a sequence of L
+ * tokens has L/kpool pools; a trailing partial pool is kept).
+ *   cu_pools_host[s] = sum over s' < s of ceil(L_s' / kpool), [nseq + 1]
+ *   *max_pools_out   = the largest pool count of one sequence (nullable)
+ * Returns the total pool count P_tot (>= 0) or a negative kpool_status. */
+int64_t kpool_count_pools(const int32_t *cu_seqlens_host, int32_t nseq, int32_t kpool,
+                          int32_t *cu_pools_host, int32_t *max_pools_out);
+
+/* Step 1 - pooled keys (Megatron-LM PR #8299 "Mechanism": rows score the
+ * pooled keys).  For pool p of sequence s, with n = min(kpool, L_s - p*kpool):
+ *   kp[cu_pools[s] + p, d] = bf16_rne( fp32( (sum_j k[cu_seqlens[s] + p*kpool + j, d]) / n ) )
+ * where the sum is taken in fp32 in token order starting from +0.
+ *   k   bf16 [T, D]  one key per token (the indexer's key projection has no head axis)
+ *   kp  bf16 [P_tot, D] output, P_tot from kpool_count_pools
+ * D must be a multiple of 8 (<= 1024); kpool >= 1. */
+int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host,
+                    const int32_t *cu_seqlens_dev, const int32_t *cu_pools_dev,
+                    int32_t nseq, int32_t D, int32_t kpool, uint16_t *kp, void *stream);
+
+/* Workspace for kpool_score_topk over rows [q_lo, q_hi): one fp32 score row
+ * per query row, at a row pitch of max_pools rounded up to 64, capped at
+ * 2 GiB per chunk (Megatron-LM PR #8299 "Change": the chunked score path
+ * caps its score buffer at 2 GiB).  Returns 0 for an empty range. */
+size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools);
+
+/* Step 2 - score and select, for the global rows [q_lo, q_hi).
+ * (Megatron-LM PR #8299 "Change": one rank's contiguous slice of query rows
+ * goes through the chunked score/top-k path; per row the result equals the
+ * unsliced one.  Atlas tp.rs module doc: the score formula and tie-break.)
+ *   q        bf16 [T, H, D]    index queries
+ *   kp       bf16 [P_tot, D]   pooled keys from kpool_pool_keys
+ *   w        fp32 [T, H]       per-row head weights (any sign)
+ *   scale    > 0, usually 1/sqrt(D)
+ *   budget   pools kept per row, 1..1024 (index_topk / kpool)
+ *   workspace, workspace_bytes: device scratch of at least one score row
+ *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools)); rows are
+ *            processed in chunks of min(2 GiB, workspace_bytes) / pitch.
+ *   pool_ids int32 [q_hi - q_lo, budget] output: sequence-local pool ids,
+ *            best first by (score desc, pool asc), -1 after the visible pools
+ *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.
+ *   scores_out NULLABLE fp32 [q_hi - q_lo, max_pools]: the fp32 scores the
+ *            selection ranked, -inf where the pool is not visible.
+ * Supported (H, D): (4, 16) and (32, 128).  q_lo == q_hi is a no-op. */
+int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
+                     const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                     int32_t nseq, int32_t H, int32_t D, int32_t kpool, float scale,
+                     int64_t q_lo, int64_t q_hi, int32_t budget,
+                     void *workspace, size_t workspace_bytes,
+                     int32_t *pool_ids, float *scores_out, void *stream);
+
+/* Step 3 - expansion and causal filter (Megatron-LM PR #8299 "Change": pool
+ * expansion and mask filtering run after the pool ids are known).
+ *   token_ids[i - q_lo, b*kpool + j] = p*kpool + j   if p = pool_ids[i - q_lo, b] >= 0
+ *                                                    and p*kpool + j <= t(i)
+ *                                    = -1            otherwise
+ *   pool_ids  int32 [q_hi - q_lo, budget];  token_ids int32 [q_hi - q_lo, budget*kpool]. */
+int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host,
+                 const int32_t *cu_seqlens_dev, int32_t nseq, int32_t kpool,
+                 int64_t q_lo, int64_t q_hi, int32_t budget, int32_t *token_ids,
+                 void *stream);
+
+/* The selection step alone, over caller-provided fp32 scores (the second
+ * half of the chunk loop, exposed so it can be checked on its own).
+ *   scores   fp32 [rows, ld], ld % 4 == 0, 16-byte aligned
+ *   n_valid  int32 [rows] device: row r ranks scores[r, 0 .. n_valid[r]),
+ *            0 <= n_valid[r] <= ld
+ *   pool_ids int32 [rows, budget]: same ordering and padding as kpool_score_topk */
+int kpool_topk(const float *scores, int64_t ld, const int32_t *n_valid, int64_t rows,
+               int32_t budget, int32_t *pool_ids, void *stream);
+
+/* Optional per-kernel device timing.  While enabled, every launch made by the
+ * library is bracketed by HIP events on its stream.  kpool_profile_collect
+ * waits for the recorded events, adds each kernel kind's elapsed time (ms)
+ * and launch count into ms[kind] / launches[kind] (arrays of
+ * KPOOL_PROFILE_KINDS) and forgets the records.  Not thread-safe. */
+#define KPOOL_PROFILE_KINDS 5 /* 0 pool_keys, 1 score, 2 topk, 3 expand, 4 scores_out copy */
+int kpool_profile_enable(int on);
+int kpool_profile_collect(double *ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KPOOL_H */

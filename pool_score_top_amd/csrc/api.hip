@@ -1,0 +1,298 @@
+// C ABI of libkpool: argument validation, chunk planning and launches.
+//
+// Pages: Megatron-LM PR #8299, "Change" -- a contiguous range of query rows is
+// scored and selected through a chunk loop whose fp32 score buffer is capped
+// at 2 GiB per chunk; the selections are int32 pool ids; expansion and mask
+// filtering follow.  This file is that loop for one GPU: [q_lo, q_hi) is the
+// one-GPU form of a rank's query slice.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/kpool.h"
+#include "kpool_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return KPOOL_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kChunkCapBytes = int64_t(1) << 31;  // 2 GiB of fp32 scores per chunk
+constexpr int kPoolSegMax = 2048;                     // pools per score workgroup (max)
+
+int64_t pitch_of(int32_t max_pools) { return (int64_t)(max_pools + 63) / 64 * 64; }
+
+// cu_seqlens_host: nseq >= 1 entries + 1, starts at 0, non-decreasing.
+int check_cu(const int32_t *cu, int32_t nseq, const char *fn) {
+  if (!cu) return fail(KPOOL_EINVAL, "%s: cu_seqlens_host is null", fn);
+  if (nseq < 1) return fail(KPOOL_EINVAL, "%s: nseq must be >= 1 (got %d)", fn, nseq);
+  if (cu[0] != 0) return fail(KPOOL_EINVAL, "%s: cu_seqlens[0] must be 0 (got %d)", fn, cu[0]);
+  for (int32_t s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s])
+      return fail(KPOOL_EINVAL, "%s: cu_seqlens must be non-decreasing (cu[%d]=%d > cu[%d]=%d)",
+                  fn, s, cu[s], s + 1, cu[s + 1]);
+  return KPOOL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing with HIP events on the launch stream.
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+template <class F>
+hipError_t timed(int kind, hipStream_t stream, F &&launch) {
+  if (!g_prof_on) return launch();
+  ProfRec rec{kind, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&rec.a);
+  if (e == hipSuccess) e = hipEventCreate(&rec.b);
+  if (e == hipSuccess) e = hipEventRecord(rec.a, stream);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(rec.b, stream);
+  if (e == hipSuccess) g_prof.push_back(rec);
+  return e;
+}
+
+int hip_fail(const char *fn, hipError_t e) {
+  return fail(KPOOL_EHIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kpool_last_error(void) { return g_err.c_str(); }
+
+int kpool_version(void) { return 100; }
+
+int64_t kpool_count_pools(const int32_t *cu_seqlens_host, int32_t nseq, int32_t kpool,
+                          int32_t *cu_pools_host, int32_t *max_pools_out) {
+  int rc = check_cu(cu_seqlens_host, nseq, "kpool_count_pools");
+  if (rc) return rc;
+  if (kpool < 1) return fail(KPOOL_EINVAL, "kpool_count_pools: kpool must be >= 1 (got %d)", kpool);
+  int64_t tot = 0;
+  int32_t mx = 0;
+  if (cu_pools_host) cu_pools_host[0] = 0;
+  for (int32_t s = 0; s < nseq; ++s) {
+    const int64_t L = (int64_t)cu_seqlens_host[s + 1] - cu_seqlens_host[s];
+    const int64_t np = (L + kpool - 1) / kpool;
+    tot += np;
+    mx = std::max<int32_t>(mx, (int32_t)np);
+    if (cu_pools_host) cu_pools_host[s + 1] = (int32_t)tot;
+  }
+  if (max_pools_out) *max_pools_out = mx;
+  ok();
+  return tot;
+}
+
+int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                    const int32_t *cu_pools_dev, int32_t nseq, int32_t D, int32_t kpool, uint16_t *kp,
+                    void *stream) {
+  const char *fn = "kpool_pool_keys";
+  int rc = check_cu(cu_seqlens_host, nseq, fn);
+  if (rc) return rc;
+  if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
+  if (D < 8 || D > 1024 || D % 8) return fail(KPOOL_EINVAL, "%s: D must be a multiple of 8 in [8, 1024] (got %d)", fn, D);
+  const int64_t P_tot = kpool_count_pools(cu_seqlens_host, nseq, kpool, nullptr, nullptr);
+  if (P_tot < 0) return (int)P_tot;
+  if (P_tot == 0) return ok();
+  if (!k || !kp || !cu_seqlens_dev || !cu_pools_dev) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
+  if (!aligned16(k) || !aligned16(kp)) return fail(KPOOL_EINVAL, "%s: k and kp must be 16-byte aligned", fn);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(0, st, [&] {
+    return kpool::launch_pool_keys(k, cu_seqlens_dev, cu_pools_dev, nseq, D, kpool, P_tot, kp, st);
+  });
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools) {
+  if (q_hi <= q_lo || max_pools <= 0) return 0;
+  const int64_t row_bytes = pitch_of(max_pools) * 4;
+  const int64_t cap_rows = std::max<int64_t>(1, kChunkCapBytes / row_bytes);
+  return (size_t)(std::min<int64_t>(q_hi - q_lo, cap_rows) * row_bytes);
+}
+
+int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
+                     const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev, int32_t nseq,
+                     int32_t H, int32_t D, int32_t kpool, float scale, int64_t q_lo, int64_t q_hi,
+                     int32_t budget, void *workspace, size_t workspace_bytes, int32_t *pool_ids,
+                     float *scores_out, void *stream) {
+  const char *fn = "kpool_score_topk";
+  int rc = check_cu(cu_seqlens_host, nseq, fn);
+  if (rc) return rc;
+  const int64_t T = cu_seqlens_host[nseq];
+  if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
+  if (budget < 1 || budget > kpool::kTopkMaxBudget)
+    return fail(KPOOL_EINVAL, "%s: budget must be in [1, %d] (got %d)", fn, kpool::kTopkMaxBudget, budget);
+  if (!(scale > 0.0f) || !isfinite(scale)) return fail(KPOOL_EINVAL, "%s: scale must be finite and > 0", fn);
+  if (q_lo < 0 || q_lo > q_hi || q_hi > T)
+    return fail(KPOOL_EINVAL, "%s: need 0 <= q_lo <= q_hi <= T (q_lo=%lld q_hi=%lld T=%lld)", fn,
+                (long long)q_lo, (long long)q_hi, (long long)T);
+  if (!kpool::score_supported(H, D))
+    return fail(KPOOL_EUNSUPPORTED, "%s: (H=%d, D=%d) not compiled; supported (4,16) and (32,128)", fn, H, D);
+  if (q_lo == q_hi) return ok();
+  if (!q || !kp || !w || !cu_seqlens_dev || !pool_ids) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
+  if (!aligned16(q) || !aligned16(kp) || !aligned16(w))
+    return fail(KPOOL_EINVAL, "%s: q, kp and w must be 16-byte aligned", fn);
+
+  std::vector<int32_t> cu_pools(nseq + 1);
+  int32_t max_pools = 0;
+  kpool_count_pools(cu_seqlens_host, nseq, kpool, cu_pools.data(), &max_pools);
+  const int64_t ld = pitch_of(max_pools);
+  const int64_t row_bytes = ld * 4;
+  if (!workspace || (int64_t)workspace_bytes < row_bytes)
+    return fail(KPOOL_EWORKSPACE, "%s: workspace must hold one score row (%lld bytes), got %zu", fn,
+                (long long)row_bytes, workspace_bytes);
+  if (!aligned16(workspace)) return fail(KPOOL_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  const int64_t chunk_rows =
+      std::max<int64_t>(1, std::min<int64_t>(kChunkCapBytes, (int64_t)workspace_bytes) / row_bytes);
+  float *ws = (float *)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  const int tile_rows = kpool::score_tile_rows();
+
+  for (int64_t c0 = q_lo; c0 < q_hi; c0 += chunk_rows) {
+    const int64_t c1 = std::min(q_hi, c0 + chunk_rows);
+    // sequences overlapping [c0, c1): one segment each, cut into row tiles
+    struct Seg { int32_t lo, hi, start, pool_base; };
+    std::vector<Seg> segs;
+    int s = (int)(std::upper_bound(cu_seqlens_host, cu_seqlens_host + nseq + 1, (int32_t)c0) -
+                  cu_seqlens_host) - 1;
+    for (; s < nseq && cu_seqlens_host[s] < c1; ++s) {
+      const int64_t lo = std::max<int64_t>(c0, cu_seqlens_host[s]);
+      const int64_t hi = std::min<int64_t>(c1, cu_seqlens_host[s + 1]);
+      if (lo < hi) segs.push_back({(int32_t)lo, (int32_t)hi, cu_seqlens_host[s], cu_pools[s]});
+    }
+    for (size_t g0 = 0; g0 < segs.size(); g0 += kpool::kMaxSegs) {
+      kpool::SegList L{};
+      int32_t ntiles = 0, max_npv = 0;
+      for (size_t g = g0; g < std::min(segs.size(), g0 + kpool::kMaxSegs); ++g) {
+        const Seg &sg = segs[g];
+        const int j = L.nseg++;
+        L.tile_start[j] = ntiles;
+        L.row_lo[j] = sg.lo;
+        L.row_hi[j] = sg.hi;
+        L.seq_start[j] = sg.start;
+        L.pool_base[j] = sg.pool_base;
+        ntiles += (sg.hi - sg.lo + tile_rows - 1) / tile_rows;
+        max_npv = std::max<int32_t>(max_npv, (sg.hi - 1 - sg.start) / kpool + 1);
+      }
+      L.tile_start[L.nseg] = ntiles;
+      // pool segments per tile: enough workgroups to fill the chip, at most kPoolSegMax pools each
+      const int64_t want_segs = std::max<int64_t>(1, (1024 + ntiles - 1) / ntiles);
+      int64_t pseg = (max_npv + want_segs - 1) / want_segs;
+      pseg = std::min<int64_t>(kPoolSegMax, std::max<int64_t>(64, (pseg + 63) / 64 * 64));
+      const int32_t npseg = (int32_t)((max_npv + pseg - 1) / pseg);
+      hipError_t e = timed(1, st, [&] {
+        return kpool::launch_score(H, D, q, kp, w, scale, kpool, L, ntiles, npseg, (int32_t)pseg,
+                                   c0, ld, ws, st);
+      });
+      if (e != hipSuccess) return hip_fail(fn, e);
+    }
+    hipError_t e = timed(2, st, [&] {
+      return kpool::launch_topk(ws, ld, c1 - c0, nullptr, cu_seqlens_dev, nseq, c0, kpool, budget,
+                                pool_ids + (c0 - q_lo) * budget, st);
+    });
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (scores_out) {
+      e = timed(4, st, [&] {
+        return kpool::launch_scores_copy(ws, ld, c1 - c0, cu_seqlens_dev, nseq, c0, kpool,
+                                         scores_out + (c0 - q_lo) * max_pools, max_pools, st);
+      });
+      if (e != hipSuccess) return hip_fail(fn, e);
+    }
+  }
+  return ok();
+}
+
+int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                 int32_t nseq, int32_t kpool, int64_t q_lo, int64_t q_hi, int32_t budget,
+                 int32_t *token_ids, void *stream) {
+  const char *fn = "kpool_expand";
+  int rc = check_cu(cu_seqlens_host, nseq, fn);
+  if (rc) return rc;
+  const int64_t T = cu_seqlens_host[nseq];
+  if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
+  if (budget < 1) return fail(KPOOL_EINVAL, "%s: budget must be >= 1 (got %d)", fn, budget);
+  if (q_lo < 0 || q_lo > q_hi || q_hi > T)
+    return fail(KPOOL_EINVAL, "%s: need 0 <= q_lo <= q_hi <= T", fn);
+  if (q_lo == q_hi) return ok();
+  if (!pool_ids || !token_ids || !cu_seqlens_dev) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
+  if (kpool == 4 && !aligned16(token_ids)) return fail(KPOOL_EINVAL, "%s: token_ids must be 16-byte aligned", fn);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(3, st, [&] {
+    return kpool::launch_expand(pool_ids, cu_seqlens_dev, nseq, kpool, q_lo, q_hi - q_lo, budget,
+                                token_ids, st);
+  });
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+int kpool_topk(const float *scores, int64_t ld, const int32_t *n_valid, int64_t rows, int32_t budget,
+               int32_t *pool_ids, void *stream) {
+  const char *fn = "kpool_topk";
+  if (rows < 0) return fail(KPOOL_EINVAL, "%s: rows must be >= 0", fn);
+  if (budget < 1 || budget > kpool::kTopkMaxBudget)
+    return fail(KPOOL_EINVAL, "%s: budget must be in [1, %d] (got %d)", fn, kpool::kTopkMaxBudget, budget);
+  if (ld < 0 || ld % 4) return fail(KPOOL_EINVAL, "%s: ld must be a non-negative multiple of 4", fn);
+  if (rows == 0) return ok();
+  if (!scores || !n_valid || !pool_ids) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
+  if (!aligned16(scores)) return fail(KPOOL_EINVAL, "%s: scores must be 16-byte aligned", fn);
+  if (rows > 0x7FFFFFFF) return fail(KPOOL_EINVAL, "%s: too many rows", fn);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(2, st, [&] {
+    return kpool::launch_topk(scores, ld, rows, n_valid, nullptr, 0, 0, 1, budget, pool_ids, st);
+  });
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
+int kpool_profile_enable(int on) {
+  g_prof_on = on != 0;
+  return ok();
+}
+
+int kpool_profile_collect(double *ms, int64_t *launches) {
+  int rc = KPOOL_OK;
+  for (ProfRec &r : g_prof) {
+    float t = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess && rc == KPOOL_OK) rc = hip_fail("kpool_profile_collect", e);
+    if (ms) ms[r.kind] += t;
+    if (launches) launches[r.kind] += 1;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  if (rc == KPOOL_OK) ok();
+  return rc;
+}
+
+}  // extern "C"

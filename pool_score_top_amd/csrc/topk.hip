@@ -1,0 +1,344 @@
+// Per-row top-k over fp32 score rows with the deterministic tie-break.
+//
+// Pages: Atlas inference glm5next_dsa/tp.rs module doc (the selection keeps
+// the higher score and, on equal scores, the smaller pool index, because a
+// library top-k leaves tie order undefined); Megatron-LM PR #8299 "Change"
+// (int32 pool ids, budget = index_topk / kpool pools per row).
+//
+// Each element is ranked by the 64-bit key (order_key(score) << 32 | ~index):
+// a larger key is better, and keys are unique, so "the best `budget` keys" is
+// exactly the selection.  One 1024-thread workgroup owns one row:
+//
+//   pass 1  (HBM)   every thread takes the max key of its elements.  In each
+//                   wave the ceil(budget/16)-th largest of the 64 maxima is
+//                   found by a register bitonic sort; the minimum L over the 16
+//                   waves is a lower bound on the budget-th best key (at least
+//                   budget distinct elements reach it).
+//   pass 2  (L2)    elements with key >= L are appended to an LDS candidate
+//                   list with one atomic per wave per step.  For iid scores the
+//                   list holds about 0.7 x 1024 + budget/2 entries, whatever the
+//                   row length.
+//   sort            bitonic sort of the candidates (descending 64-bit keys):
+//                   distances < 64 via lane shuffles, < 1024 via LDS, larger
+//                   inside a thread's registers; the first `budget` are written.
+//   fallback        if the list overflows (heavy ties), an exact radix select
+//                   over the 64-bit keys (8-bit digits, re-reading the row)
+//                   finds the budget-th key and collects exactly budget
+//                   elements, which are then sorted the same way.
+// Rows with no more than `budget` elements skip the bound and keep them all;
+// unused output slots are -1.
+#include "kpool_internal.h"
+
+namespace kpool {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWavesT = kThreads / 64;
+constexpr int kCandCap = 4096;
+
+__device__ inline uint64_t compose(uint32_t okey, uint32_t idx) {
+  return ((uint64_t)okey << 32) | (uint64_t)(~idx);
+}
+
+__device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = __shfl_xor((unsigned)(uint32_t)v, mask);
+  const uint32_t hi = __shfl_xor((unsigned)(uint32_t)(v >> 32), mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// 64 values of a wave sorted descending; lane r returns the r-th largest.
+__device__ inline uint32_t wave_sort_desc(uint32_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t p = __shfl_xor(v, j);
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & k) == 0;
+      v = (lower == desc) ? max(v, p) : min(v, p);
+    }
+  }
+  return v;
+}
+
+// Bitonic sort (descending) of 1024*M keys; thread tid holds elements
+// tid + 1024*m.  buf is an LDS scratch of 1024*M keys.
+template <int M>
+__device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
+  constexpr int N = kThreads * M;
+#pragma unroll 1
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll 1
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kThreads) {
+        const int jm = j / kThreads;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          if ((m & jm) == 0) {
+            const int m2 = m | jm;
+            const bool desc = ((tid + kThreads * m) & k) == 0;
+            const uint64_t a = v[m], b = v[m2];
+            if (desc ? (a < b) : (a > b)) { v[m] = b; v[m2] = a; }
+          }
+        }
+      } else if (j >= 64) {
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M; ++m) buf[tid + kThreads * m] = v[m];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int i = tid + kThreads * m;
+          const uint64_t p = buf[i ^ j];
+          const bool lower = (i & j) == 0;
+          const bool desc = (i & k) == 0;
+          v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int i = tid + kThreads * m;
+          const uint64_t p = shfl_xor_u64(v[m], j);
+          const bool lower = (i & j) == 0;
+          const bool desc = (i & k) == 0;
+          v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
+        }
+      }
+    }
+  }
+}
+
+template <int M>
+__device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32_t *orow, int tid) {
+  uint64_t v[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t i = tid + kThreads * m;
+    v[m] = i < count ? cand[i] : 0ull;  // 0 is below every real key
+  }
+  block_sort_desc<M>(v, cand, tid);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int i = tid + kThreads * m;
+    if (i < budget) orow[i] = (v[m] != 0ull) ? (int32_t)(~(uint32_t)v[m]) : -1;
+  }
+}
+
+struct Smem {
+  uint64_t cand[kCandCap];
+  uint32_t hist[256];
+  uint32_t wave_bound[kWavesT];
+  uint64_t prefix;
+  uint32_t count;
+  int32_t pbits;
+  int32_t krem;
+  int32_t done;
+};
+
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
+                                                        const int32_t *__restrict__ n_valid,
+                                                        const int32_t *__restrict__ cu_seqlens,
+                                                        int nseq, int64_t grow0, int kpool,
+                                                        int budget, int32_t *__restrict__ out) {
+  __shared__ Smem sm;
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int64_t n;
+  if (n_valid) {
+    n = min<int64_t>(max<int64_t>(n_valid[r], 0), ld);
+  } else {
+    const int64_t i = grow0 + r;
+    const int s = find_seq(cu_seqlens, nseq, i);
+    n = (i - cu_seqlens[s]) / kpool + 1;
+  }
+  const float *row = scores + r * ld;
+  int32_t *orow = out + r * (int64_t)budget;
+  if (tid == 0) sm.count = 0;
+
+  // ---- pass 1: lower bound on the budget-th best key ----------------------
+  uint32_t bound = 0;
+  if (n > budget) {
+    uint32_t tmax = 0;
+    for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
+      const int64_t base = wbase + 4 * lane;
+      if (base < n) {
+        const float4 x = *reinterpret_cast<const float4 *>(row + base);
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (base + e < n) tmax = max(tmax, order_key(xs[e]));
+      }
+    }
+    const uint32_t sorted = wave_sort_desc(tmax, lane);
+    const int rank = (budget + kWavesT - 1) / kWavesT;
+    const uint32_t wb = __shfl(sorted, rank - 1);
+    if (lane == 0) sm.wave_bound[wave] = wb;
+    __syncthreads();
+    bound = sm.wave_bound[0];
+#pragma unroll
+    for (int w = 1; w < kWavesT; ++w) bound = min(bound, sm.wave_bound[w]);
+  }
+  __syncthreads();
+
+  // ---- pass 2: gather candidates with key >= bound ------------------------
+  for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
+    const int64_t base = wbase + 4 * lane;
+    uint32_t keys[4] = {0, 0, 0, 0};
+    bool sel[4] = {false, false, false, false};
+    uint32_t c = 0;
+    if (base < n) {
+      const float4 x = *reinterpret_cast<const float4 *>(row + base);
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        keys[e] = order_key(xs[e]);
+        sel[e] = (base + e < n) && keys[e] >= bound;
+        c += sel[e] ? 1u : 0u;
+      }
+    }
+    const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+    const uint32_t tot = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
+    if (tot) {
+      const uint32_t pre =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u)) +
+          2u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u)) +
+          4u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0u));
+      uint32_t wbase_pos = 0;
+      if (lane == 0) wbase_pos = atomicAdd(&sm.count, tot);
+      wbase_pos = __shfl(wbase_pos, 0);
+      uint32_t pos = wbase_pos + pre;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (sel[e]) {
+          if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base + e));
+          ++pos;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t count = sm.count;
+
+  // ---- fallback: exact radix select when the candidate list overflowed ----
+  if (count > (uint32_t)kCandCap) {
+    uint64_t prefix = 0;
+    int pbits = 0;
+    int krem = budget;
+    // keys are unique, so the bin holds exactly krem keys after at most 8 digits
+    for (int pass = 0; pass < 8; ++pass) {
+      if (tid < 256) sm.hist[tid] = 0;
+      __syncthreads();
+      for (int64_t base = 4 * (int64_t)tid; base < n; base += kThreads * 4) {
+        const float4 x = *reinterpret_cast<const float4 *>(row + base);
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (base + e < n) {
+            const uint64_t ck = compose(order_key(xs[e]), (uint32_t)(base + e));
+            if (pbits == 0 || (ck >> (64 - pbits)) == prefix)
+              atomicAdd(&sm.hist[(uint32_t)(ck >> (56 - pbits)) & 255u], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t cum = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (cum + sm.hist[d] >= (uint32_t)krem) break;
+          cum += sm.hist[d];
+        }
+        sm.krem = krem - (int)cum;
+        sm.prefix = (prefix << 8) | (uint64_t)d;
+        sm.pbits = pbits + 8;
+        sm.done = (sm.hist[d] == (uint32_t)sm.krem) ? 1 : 0;
+        sm.count = 0;
+      }
+      __syncthreads();
+      prefix = sm.prefix;
+      pbits = sm.pbits;
+      krem = sm.krem;
+      if (sm.done) break;
+    }
+    // exactly `budget` keys have their top pbits >= prefix
+    for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
+      const int64_t base = wbase + 4 * lane;
+      uint64_t cks[4] = {0, 0, 0, 0};
+      bool sel[4] = {false, false, false, false};
+      uint32_t c = 0;
+      if (base < n) {
+        const float4 x = *reinterpret_cast<const float4 *>(row + base);
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          cks[e] = compose(order_key(xs[e]), (uint32_t)(base + e));
+          sel[e] = (base + e < n) && ((pbits >= 64 ? cks[e] : (cks[e] >> (64 - pbits))) >= prefix);
+          c += sel[e] ? 1u : 0u;
+        }
+      }
+      const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+      const uint32_t tot = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
+      if (tot) {
+        const uint32_t pre =
+            __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u)) +
+            2u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u)) +
+            4u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0u));
+        uint32_t wbase_pos = 0;
+        if (lane == 0) wbase_pos = atomicAdd(&sm.count, tot);
+        wbase_pos = __shfl(wbase_pos, 0);
+        uint32_t pos = wbase_pos + pre;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (sel[e]) {
+            if (pos < (uint32_t)kCandCap) sm.cand[pos] = cks[e];
+            ++pos;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    count = min(sm.count, (uint32_t)kCandCap);
+  }
+
+  if (count <= 1024u) sort_and_write<1>(sm.cand, count, budget, orow, tid);
+  else if (count <= 2048u) sort_and_write<2>(sm.cand, count, budget, orow, tid);
+  else sort_and_write<4>(sm.cand, count, budget, orow, tid);
+}
+
+// scores_out rows: the chunk buffer's visible scores, -inf elsewhere
+__global__ __launch_bounds__(256) void scores_copy_kernel(const float *__restrict__ ws, int64_t ld,
+                                                          const int32_t *__restrict__ cu_seqlens,
+                                                          int nseq, int64_t grow0, int kpool,
+                                                          float *__restrict__ dst, int64_t dst_ld) {
+  const int64_t r = blockIdx.x;
+  const int64_t i = grow0 + r;
+  const int s = find_seq(cu_seqlens, nseq, i);
+  const int64_t n = (i - cu_seqlens[s]) / kpool + 1;
+  const float ninf = __uint_as_float(0xFF800000u);
+  for (int64_t p = threadIdx.x; p < dst_ld; p += blockDim.x)
+    dst[r * dst_ld + p] = p < n ? ws[r * ld + p] : ninf;
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
+                       const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
+                       int32_t budget, int32_t *out, hipStream_t stream) {
+  if (nrows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)nrows), dim3(kThreads), 0, stream, scores, ld,
+                     n_valid, cu_seqlens, nseq, grow0, kpool, budget, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores_copy(const float *ws, int64_t ld, int64_t nrows, const int32_t *cu_seqlens,
+                              int32_t nseq, int64_t grow0, int32_t kpool, float *dst,
+                              int64_t dst_ld, hipStream_t stream) {
+  if (nrows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scores_copy_kernel, dim3((unsigned)nrows), dim3(256), 0, stream, ws, ld,
+                     cu_seqlens, nseq, grow0, kpool, dst, dst_ld);
+  return hipGetLastError();
+}
+
+}  // namespace kpool

@@ -1,0 +1,146 @@
+"""Shared helpers for the GPU parity tests (comparison rules and runners).
+
+Comparison rules (GPU vs the fp64 CPU oracle):
+  * pooled keys: bit-identical.
+  * scores: every visible (row, pool) within |g - o| <= ATOL + RTOL*|o|;
+    masked entries exactly -inf.
+  * selection vs its own scores: the GPU ids are exactly the first `budget`
+    pools of the GPU's fp32 scores ordered by (score desc, index asc), -0 == +0,
+    -1 padded (checked here with a plain lexsort, a property of the output).
+  * selection vs the oracle: the id sets may differ only in pools whose
+    oracle score lies within tolerance of the row's cutoff, and the GPU order
+    may only swap pools whose oracle scores are within tolerance.
+  * token ids: equal to the oracle's where the pool ids are, and the expansion
+    rule holds on every row.
+"""
+import numpy as np
+import torch
+
+import oracle
+from pool_score_top_amd import kpool as K
+from pool_score_top_amd import synth
+
+RTOL = 1e-3
+ATOL = 1e-4
+
+
+def tol(o):
+    return ATOL + RTOL * np.abs(o)
+
+
+def device_tensors(inputs, device="cuda"):
+    q = torch.from_numpy(inputs["q"].view(np.int16)).to(device)
+    k = torch.from_numpy(inputs["k"].view(np.int16)).to(device)
+    w = torch.from_numpy(inputs["w"]).to(device)
+    return q, k, w
+
+
+def run_gpu(inputs, kpool, budget, q_lo=0, q_hi=None, want_scores=True, workspace_cap=None):
+    cu = np.asarray(inputs["cu_seqlens"], dtype=np.int32)
+    q, k, w = device_tensors(inputs)
+    H, D = inputs["q"].shape[1:]
+    sel = K.Selector(cu, kpool, budget, H, D, q_lo=q_lo, q_hi=q_hi, workspace_cap=workspace_cap)
+    scores = None
+    if want_scores:
+        scores = torch.empty((sel.q_hi - sel.q_lo, sel.max_pools), dtype=torch.float32, device="cuda")
+    out = sel.run(q, k, w, scores_out=scores)
+    torch.cuda.synchronize()
+    res = {
+        "kp": out["kp"].cpu().numpy().view(np.uint16),
+        "pool_ids": out["pool_ids"].cpu().numpy(),
+        "token_ids": out["token_ids"].cpu().numpy(),
+        "scores": None if scores is None else scores.cpu().numpy(),
+        "max_pools": sel.max_pools,
+    }
+    return res
+
+
+def lexsort_first(scores_f32, budget):
+    """First `budget` indices of the (score desc, index asc) order of fp32 scores."""
+    s = np.asarray(scores_f32, dtype=np.float64) + 0.0
+    isnan = np.isnan(s)
+    s = np.where(isnan, -np.inf, s)
+    idx = np.arange(len(s))
+    order = np.lexsort((idx, -s, isnan))[:budget]
+    out = np.full(budget, -1, dtype=np.int32)
+    out[:len(order)] = order
+    return out
+
+
+def check_scores(g, o, nvis, where=""):
+    """g: fp32 [rows, width] GPU scores, o: fp64 oracle scores, nvis: visible per row."""
+    for r in range(len(nvis)):
+        n = int(nvis[r])
+        d = np.abs(g[r, :n].astype(np.float64) - o[r, :n])
+        bad = d > tol(o[r, :n])
+        assert not bad.any(), (f"{where} row {r}: {bad.sum()} scores out of tolerance, "
+                               f"max err {d.max():.3e}")
+        assert np.all(np.isneginf(g[r, n:])), f"{where} row {r}: masked scores not -inf"
+
+
+def check_topk_self(g_scores, g_ids, nvis, budget, where=""):
+    for r in range(len(nvis)):
+        want = lexsort_first(g_scores[r, :int(nvis[r])], budget)
+        if not np.array_equal(want, g_ids[r]):
+            bad = np.nonzero(want != g_ids[r])[0][:5]
+            raise AssertionError(f"{where} row {r}: top-k differs from its own scores at slots "
+                                 f"{bad.tolist()}: gpu {g_ids[r][bad].tolist()} want {want[bad].tolist()}")
+
+
+def check_selection_vs_oracle(g_ids, o_scores, nvis, budget, where=""):
+    """Set and order agreement with the fp64 oracle, up to pools tied within tolerance."""
+    worst = 0.0
+    for r in range(len(nvis)):
+        n = int(nvis[r])
+        o = o_scores[r, :n]
+        ids = g_ids[r]
+        sel = ids[ids >= 0]
+        assert len(sel) == min(n, budget), f"{where} row {r}: {len(sel)} ids, want {min(n, budget)}"
+        assert np.all(ids[len(sel):] == -1), f"{where} row {r}: padding not at the tail"
+        assert len(np.unique(sel)) == len(sel), f"{where} row {r}: duplicate ids"
+        assert sel.max() < n, f"{where} row {r}: id beyond the visible pools"
+        want = oracle.select_row(o, budget)
+        want = want[want >= 0]
+        if n <= budget:
+            assert set(sel.tolist()) == set(range(n)), f"{where} row {r}: not every visible pool"
+        else:
+            c = np.sort(o)[::-1][budget - 1]
+            diff = np.setxor1d(sel, want)
+            if len(diff):
+                err = np.abs(o[diff] - c)
+                worst = max(worst, float(err.max()))
+                assert np.all(err <= tol(c)), (f"{where} row {r}: pools {diff[err > tol(c)][:5]} "
+                                               f"differ from the oracle away from the cutoff")
+        # order: oracle scores non-increasing along the GPU order, within tolerance
+        os_ = o[sel]
+        drops = os_[1:] - os_[:-1]
+        assert np.all(drops <= tol(os_[:-1])), f"{where} row {r}: order disagrees with the oracle"
+    return worst
+
+
+def check_tokens(g_tok, g_ids, t, kpool, o_ids=None, o_tok=None, where=""):
+    """Token ids: equal to the oracle's where the pool ids agree with it, and for every row
+    slot b*kpool+j holds p*kpool+j for p = ids[b] >= 0 with p*kpool+j <= t, else -1."""
+    t = np.asarray(t, dtype=np.int64)
+    p = np.repeat(g_ids.astype(np.int64), kpool, axis=1)
+    j = np.tile(np.arange(kpool), g_ids.shape[1])[None, :]
+    tok = p * kpool + j
+    want = np.where((p >= 0) & (tok <= t[:, None]), tok, -1)
+    bad = np.nonzero((g_tok != want).any(axis=1))[0]
+    assert len(bad) == 0, f"{where} rows {bad[:5].tolist()}: token ids break the expansion rule"
+    if o_ids is not None:
+        same = (g_ids == o_ids).all(axis=1)
+        assert np.array_equal(g_tok[same], o_tok[same]), f"{where}: token ids differ from the oracle"
+
+
+def oracle_rows(inputs, kpool, rows, kp=None, width=None):
+    """fp64 oracle scores for the given global rows (and the pooled keys)."""
+    cu = np.asarray(inputs["cu_seqlens"])
+    if kp is None:
+        kp = oracle.pool_keys(inputs["k"], cu, kpool)
+    cu_pools, max_pools = oracle.count_pools(cu, kpool)
+    rows = np.asarray(rows)
+    seq, t = oracle.row_positions(rows, cu)
+    s = oracle.row_scores(inputs["q"][rows], inputs["w"][rows], kp, cu_pools, seq, t, kpool,
+                          width=max_pools if width is None else width)
+    return kp, s, t

@@ -1,0 +1,122 @@
+"""The C ABI without a GPU: the library loads, exports what include/kpool.h
+declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from pool_score_top_amd import kpool as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kpool.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(K.LIB_PATH), reason="libkpool.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kpool_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("kpool_pool_keys", "kpool_score_topk", "kpool_expand", "kpool_topk",
+                 "kpool_count_pools", "kpool_workspace_bytes", "kpool_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(K.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert K.version() == 100
+
+
+def test_count_pools_and_workspace():
+    cu_pools, mx, tot = K.count_pools([0, 9, 9, 37], 4)
+    assert cu_pools.tolist() == [0, 3, 3, 10] and mx == 7 and tot == 10
+    # 512k tokens, kpool 4: pitch 131072 floats = 512 KiB per row -> 4096 rows per 2 GiB chunk
+    assert K.workspace_bytes(0, 524288, 131072) == 2**31
+    assert K.workspace_bytes(0, 100, 131072) == 100 * 131072 * 4
+    assert K.workspace_bytes(5, 5, 10) == 0
+    assert K.workspace_bytes(0, 3, 1) == 3 * 64 * 4   # pitch rounds up to 64
+
+
+def _call_score(**kw):
+    L = K.lib()
+    cu = np.array(kw.pop("cu", [0, 64]), dtype=np.int32)
+    args = dict(q=16, kp=16, w=16, cu_dev=16, nseq=len(cu) - 1, H=4, D=16, kpool=4, scale=0.25,
+                q_lo=0, q_hi=int(cu[-1]), budget=4, ws=16, ws_bytes=1 << 20, ids=16)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return L.kpool_score_topk(vp(args["q"]), vp(args["kp"]), vp(args["w"]),
+                              cu.ctypes.data_as(vp), vp(args["cu_dev"]), args["nseq"], args["H"],
+                              args["D"], args["kpool"], ctypes.c_float(args["scale"]), args["q_lo"],
+                              args["q_hi"], args["budget"], vp(args["ws"]), args["ws_bytes"],
+                              vp(args["ids"]), None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_lo=5, q_hi=4), K.KPOOL_EINVAL),
+    (dict(q_hi=65), K.KPOOL_EINVAL),
+    (dict(q_lo=-1), K.KPOOL_EINVAL),
+    (dict(budget=0), K.KPOOL_EINVAL),
+    (dict(budget=1025), K.KPOOL_EINVAL),
+    (dict(kpool=0), K.KPOOL_EINVAL),
+    (dict(scale=0.0), K.KPOOL_EINVAL),
+    (dict(scale=float("nan")), K.KPOOL_EINVAL),
+    (dict(H=8), K.KPOOL_EUNSUPPORTED),
+    (dict(D=64), K.KPOOL_EUNSUPPORTED),
+    (dict(q=0), K.KPOOL_EINVAL),
+    (dict(q=8), K.KPOOL_EINVAL),            # misaligned
+    (dict(ws=0), K.KPOOL_EWORKSPACE),
+    (dict(ws_bytes=100), K.KPOOL_EWORKSPACE),  # less than one 256-byte score row
+    (dict(cu=[1, 64]), K.KPOOL_EINVAL),
+    (dict(cu=[0, 40, 30, 64]), K.KPOOL_EINVAL),
+    (dict(nseq=0), K.KPOOL_EINVAL),
+])
+def test_score_topk_rejects_bad_arguments(kw, code):
+    rc = _call_score(**kw)
+    assert rc == code
+    assert K.lib().kpool_last_error().decode()
+
+
+def test_empty_range_is_a_noop_without_pointers():
+    assert _call_score(q_lo=10, q_hi=10, q=0, kp=0, w=0, ws=0, ids=0) == K.KPOOL_OK
+
+
+def test_other_entry_points_reject_bad_arguments():
+    L = K.lib()
+    vp = ctypes.c_void_p
+    cu = np.array([0, 64], dtype=np.int32)
+    cup = cu.ctypes.data_as(vp)
+    assert L.kpool_pool_keys(vp(16), cup, vp(16), vp(16), 1, 12, 4, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_pool_keys(vp(16), cup, vp(16), vp(16), 1, 16, 0, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_pool_keys(None, cup, vp(16), vp(16), 1, 16, 4, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 3, 2, 4, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 0, 65, 4, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(None, cup, vp(16), 1, 4, 0, 64, 4, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 0, 64, 4, vp(8), None) == K.KPOOL_EINVAL
+    assert L.kpool_topk(vp(16), 6, vp(16), 3, 4, vp(16), None) == K.KPOOL_EINVAL      # ld % 4
+    assert L.kpool_topk(vp(16), 8, vp(16), 3, 0, vp(16), None) == K.KPOOL_EINVAL      # budget
+    assert L.kpool_topk(vp(8), 8, vp(16), 3, 4, vp(16), None) == K.KPOOL_EINVAL       # alignment
+    assert L.kpool_topk(None, 8, vp(16), 0, 4, None, None) == K.KPOOL_OK              # no rows
+    assert L.kpool_count_pools(cup, 1, 0, None, None) == K.KPOOL_EINVAL
+
+
+def test_shard_bounds_cover_every_row_once():
+    """The pages' per-rank bounds [r*ceil(sq/G), min(sq, (r+1)*ceil(sq/G))) partition the rows
+    (Megatron-LM PR #8299, 'Change' and 'Test plan'); the one-GPU row ranges use the same
+    arithmetic, including empty ranges when sq < G."""
+    for sq in (5, 24, 37, 4096):
+        for G in (1, 2, 3, 8):
+            per = -(-sq // G)
+            seen = np.zeros(sq, dtype=np.int64)
+            for r in range(G):
+                lo, hi = min(sq, r * per), min(sq, (r + 1) * per)
+                assert lo <= hi
+                seen[lo:hi] += 1
+            assert np.all(seen == 1)

@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Sizes here are ones the oracle finishes in seconds but that still span many
+score tiles (32 rows), LDS stages (64 pools), pool segments and top-k
+candidate sorts, with ragged tails everywhere.  Full-size workloads are
+checked on sampled rows in test_gpu_full.py.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (check_scores, check_selection_vs_oracle, check_tokens, check_topk_self,
+                         device_tensors, oracle_rows, run_gpu)
+from pool_score_top_amd import kpool as K
+from pool_score_top_amd import synth
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _inputs(name, seed=0, **over):
+    wl = synth.workload(name, **over)
+    r = synth.host_inputs(wl, seed)
+    return wl, r
+
+
+def _full_check(wl, r, res, rows=None, where=""):
+    """Every comparison rule on the given rows (default: all rows)."""
+    cu = r["cu_seqlens"]
+    if rows is None:
+        rows = np.arange(wl.T)
+    kp, o_scores, t = oracle_rows(r, wl.kpool, rows, width=res["max_pools"])
+    np.testing.assert_array_equal(res["kp"], kp)
+    nvis = t // wl.kpool + 1
+    g_scores = res["scores"][rows - 0]
+    check_scores(g_scores, o_scores, nvis, where)
+    check_topk_self(g_scores, res["pool_ids"][rows], nvis, wl.budget, where)
+    check_selection_vs_oracle(res["pool_ids"][rows], o_scores, nvis, wl.budget, where)
+    o_ids = np.stack([oracle.select_row(o_scores[i, :nvis[i]], wl.budget) for i in range(len(rows))])
+    o_tok = np.stack([oracle.expand_row(o_ids[i], int(t[i]), wl.kpool) for i in range(len(rows))])
+    check_tokens(res["token_ids"][rows], res["pool_ids"][rows], t, wl.kpool, o_ids, o_tok, where)
+    return o_ids
+
+
+# ---------------------------------------------------------------------------
+# Pooling: bit-exact
+# ---------------------------------------------------------------------------
+
+def test_pool_keys_hand_values():
+    with open(os.path.join(GOLDEN, "pool_pins.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        k1 = np.array([int(x, 16) for x in c["keys"]], dtype=np.uint16)
+        k = np.repeat(k1[:, None], 8, axis=1)          # D = 8, every column the same case
+        cu = np.array([0, len(k1)], dtype=np.int32)
+        cu_pools, _, P = K.count_pools(cu, c["kpool"])
+        kd = torch.from_numpy(k.view(np.int16)).cuda()
+        kp = K.pool_keys(kd, cu, torch.from_numpy(cu).cuda(), torch.from_numpy(cu_pools).cuda(),
+                         c["kpool"])
+        got = kp.cpu().numpy().view(np.uint16)
+        want = np.array([int(x, 16) for x in c["pooled"]], dtype=np.uint16)
+        assert np.array_equal(got, np.repeat(want[:, None], 8, axis=1)), c["name"]
+
+
+@pytest.mark.parametrize("name,seed,variant", [
+    ("tiny", 0, ""), ("sq4096", 1, ""), ("thd65536", 2, ""), ("sq4096", 3, "k_ternary"),
+])
+def test_pool_keys_bitexact(name, seed, variant):
+    wl, r = _inputs(name, seed, variant=variant)
+    cu = r["cu_seqlens"]
+    cu_pools, _, _ = K.count_pools(cu, wl.kpool)
+    kd = torch.from_numpy(r["k"].view(np.int16)).cuda()
+    kp = K.pool_keys(kd, cu, torch.from_numpy(cu).cuda(), torch.from_numpy(cu_pools).cuda(), wl.kpool)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kp.cpu().numpy().view(np.uint16), oracle.pool_keys(r["k"], cu, wl.kpool))
+
+
+@pytest.mark.parametrize("kpool", [1, 2, 3, 5])
+def test_pool_keys_other_pool_sizes(kpool):
+    wl, r = _inputs("tiny", 4, T=203)
+    cu = np.array([0, 1, 50, 50, 203], dtype=np.int32)
+    cu_pools, _, _ = K.count_pools(cu, kpool)
+    kd = torch.from_numpy(r["k"].view(np.int16)).cuda()
+    kp = K.pool_keys(kd, cu, torch.from_numpy(cu).cuda(), torch.from_numpy(cu_pools).cuda(), kpool)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kp.cpu().numpy().view(np.uint16), oracle.pool_keys(r["k"], cu, kpool))
+
+
+# ---------------------------------------------------------------------------
+# Whole path vs the oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_workload(seed):
+    wl, r = _inputs("tiny", seed)
+    res = run_gpu(r, wl.kpool, wl.budget)
+    _full_check(wl, r, res, where=f"tiny s{seed}")
+
+
+@pytest.mark.parametrize("variant", ["", "w_neg", "k_ternary", "w_zero"])
+def test_tiny_shapes_variants(variant):
+    wl, r = _inputs("tiny", 7, T=300, variant=variant)
+    r["cu_seqlens"] = np.array([0, 1, 2, 37, 37, 100, 300], dtype=np.int32)
+    for budget in (1, 4, 13):
+        res = run_gpu(r, wl.kpool, budget)
+        _full_check(synth.workload("tiny", T=300, budget=budget), r, res, where=f"{variant} b{budget}")
+
+
+def test_sq4096_workload():
+    wl, r = _inputs("sq4096", 0)
+    res = run_gpu(r, wl.kpool, wl.budget)
+    _full_check(wl, r, res, where="sq4096")
+
+
+def test_thd_workload_windows():
+    wl, r = _inputs("thd65536", 0)
+    cu = r["cu_seqlens"]
+    res = run_gpu(r, wl.kpool, wl.budget, want_scores=False)
+    # windows at every sequence start and end plus a spread of interior rows
+    rows = set()
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        rows.update(range(a, min(b, a + 6)))
+        rows.update(range(max(a, b - 6), b))
+    rows.update(np.linspace(0, wl.T - 1, 40).astype(int).tolist())
+    rows = np.array(sorted(rows))
+    # scores for those rows come from a second GPU call per row (same kernels, own range)
+    q, k, w = device_tensors(r)
+    sel = K.Selector(cu, wl.kpool, wl.budget, wl.H, wl.D)
+    kp = K.pool_keys(k, cu, sel.cu_dev, sel.cu_pools_dev, wl.kpool)
+    g_scores = np.empty((len(rows), sel.max_pools), dtype=np.float32)
+    g_ids = np.empty((len(rows), wl.budget), dtype=np.int32)
+    for i, row in enumerate(rows):
+        ids, sc = K.score_topk(q, kp, w, cu, sel.cu_dev, wl.kpool, wl.budget, int(row), int(row) + 1,
+                               want_scores=True)
+        g_scores[i] = sc.cpu().numpy()[0]
+        g_ids[i] = ids.cpu().numpy()[0]
+    np.testing.assert_array_equal(g_ids, res["pool_ids"][rows])     # row split == full run
+    kp_o, o_scores, t = oracle_rows(r, wl.kpool, rows, width=sel.max_pools)
+    np.testing.assert_array_equal(res["kp"], kp_o)
+    nvis = t // wl.kpool + 1
+    check_scores(g_scores, o_scores, nvis, "thd")
+    check_topk_self(g_scores, g_ids, nvis, wl.budget, "thd")
+    check_selection_vs_oracle(g_ids, o_scores, nvis, wl.budget, "thd")
+    check_tokens(res["token_ids"][rows], res["pool_ids"][rows], t, wl.kpool, where="thd")
+
+
+# ---------------------------------------------------------------------------
+# Invariants of the whole path
+# ---------------------------------------------------------------------------
+
+def test_row_split_and_chunking_reassemble_bitwise():
+    """Slices [q_lo, q_hi) with a workspace of a few rows (many chunks, slice edges inside
+    chunks and tiles) concatenate to the single full run, scores and ids alike
+    (Megatron-LM PR #8299, 'Test plan': sharded == unsharded, small chunk cap)."""
+    wl, r = _inputs("sq4096", 5, T=1500)
+    r["cu_seqlens"] = np.array([0, 700, 701, 1500], dtype=np.int32)
+    full = run_gpu(r, wl.kpool, 64)
+    row_bytes = ((full["max_pools"] + 63) // 64) * 64 * 4
+    for bounds, cap in [((0, 333, 334, 1000, 1500), 7 * row_bytes), ((0, 1, 700, 1499, 1500), row_bytes),
+                        ((0, 750, 1500), 100 * row_bytes)]:
+        parts = [run_gpu(r, wl.kpool, 64, q_lo=a, q_hi=b, workspace_cap=cap)
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        for key in ("pool_ids", "token_ids", "scores"):
+            np.testing.assert_array_equal(np.concatenate([p[key] for p in parts]), full[key], err_msg=key)
+
+
+def test_thd_packing_invariance():
+    wl, r = _inputs("sq4096", 6, T=2000)
+    cu = np.array([0, 333, 1200, 2000], dtype=np.int32)
+    r["cu_seqlens"] = cu
+    packed = run_gpu(r, wl.kpool, 32)
+    for s in range(3):
+        a, b = int(cu[s]), int(cu[s + 1])
+        alone = {"q": r["q"][a:b], "k": r["k"][a:b], "w": r["w"][a:b],
+                 "cu_seqlens": np.array([0, b - a], dtype=np.int32)}
+        res = run_gpu(alone, wl.kpool, 32)
+        np.testing.assert_array_equal(res["pool_ids"], packed["pool_ids"][a:b])
+        np.testing.assert_array_equal(res["token_ids"], packed["token_ids"][a:b])
+        n = res["scores"].shape[1]
+        np.testing.assert_array_equal(res["scores"], packed["scores"][a:b, :n])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    wl, r = _inputs("sq4096", 8, T=3000)
+    a = run_gpu(r, wl.kpool, wl.budget)
+    b = run_gpu(r, wl.kpool, wl.budget)
+    for key in ("kp", "pool_ids", "token_ids", "scores"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_weight_doubling_doubles_scores_exactly():
+    wl, r = _inputs("sq4096", 9, T=1000)
+    a = run_gpu(r, wl.kpool, 100)
+    r2 = dict(r)
+    r2["w"] = (r["w"] * np.float32(2)).astype(np.float32)
+    b = run_gpu(r2, wl.kpool, 100)
+    np.testing.assert_array_equal(b["scores"], 2 * a["scores"])
+    np.testing.assert_array_equal(b["pool_ids"], a["pool_ids"])
+
+
+def test_zero_weights_select_by_index():
+    wl, r = _inputs("sq4096", 0, T=3000, variant="w_zero")
+    res = run_gpu(r, wl.kpool, wl.budget)
+    for i in range(3000):
+        m = min(wl.budget, i // 4 + 1)
+        assert res["pool_ids"][i, :m].tolist() == list(range(m))
+        assert np.all(res["pool_ids"][i, m:] == -1)
+
+
+# ---------------------------------------------------------------------------
+# The selection and expansion steps on their own
+# ---------------------------------------------------------------------------
+
+def _topk_rows(rng):
+    rows = []
+    for n in (0, 1, 3, 511, 512, 513, 1000, 4095, 4096, 4097, 20000, 131072):
+        rows.append(rng.standard_normal(n).astype(np.float32))
+    rows.append(np.zeros(131072, dtype=np.float32))                                   # all tied
+    rows.append(rng.integers(-2, 3, 70000).astype(np.float32))                        # 5 values
+    x = rng.standard_normal(9000).astype(np.float32)
+    x[rng.random(9000) < 0.3] = 0.0
+    x[rng.random(9000) < 0.3] = -0.0
+    rows.append(x)                                                                    # +-0 ties
+    y = np.round(rng.random(60000), 3).astype(np.float32)
+    y[::7] = -np.inf
+    y[5::11] = np.nan
+    rows.append(y)                                                                    # inf, nan, ties
+    z = rng.standard_normal(50000).astype(np.float32)
+    z[1000:6000] = z.max() + 1.0                                                      # 5000 tied on top
+    rows.append(z)
+    ramp = np.arange(30000, dtype=np.float32)                                         # sorted input
+    rows.append(ramp)
+    rows.append(ramp[::-1].copy())
+    return rows
+
+
+@pytest.mark.parametrize("budget", [1, 7, 512, 1024])
+def test_topk_standalone_matches_oracle_selection(budget):
+    rng = np.random.default_rng(budget)
+    rows = _topk_rows(rng)
+    ld = max(len(x) for x in rows)
+    ld = (ld + 3) // 4 * 4
+    buf = np.full((len(rows), ld), np.nan, dtype=np.float32)   # junk past n_valid
+    for i, x in enumerate(rows):
+        buf[i, :len(x)] = x
+    nv = np.array([len(x) for x in rows], dtype=np.int32)
+    got = K.topk(torch.from_numpy(buf).cuda(), torch.from_numpy(nv).cuda(), budget)
+    got = got.cpu().numpy()
+    for i, x in enumerate(rows):
+        want = oracle.select_row_full_sort(x, budget)
+        assert np.array_equal(got[i], want), f"row {i} (n={len(x)})"
+
+
+def test_expand_standalone_matches_oracle():
+    rng = np.random.default_rng(3)
+    for kpool in (1, 3, 4):
+        cu = np.array([0, 5, 5, 900, 1000], dtype=np.int32)
+        T = int(cu[-1])
+        budget = 17
+        ids = rng.integers(-1, 230, size=(T, budget)).astype(np.int32)
+        got = K.expand(torch.from_numpy(ids).cuda(), cu, torch.from_numpy(cu).cuda(), kpool, budget, 0, T)
+        got = got.cpu().numpy()
+        _, t = oracle.row_positions(np.arange(T), cu)
+        for i in range(T):
+            assert np.array_equal(got[i], oracle.expand_row(ids[i], int(t[i]), kpool)), (kpool, i)
+        # a sub-range lands at offset 0 of its own output
+        sub = K.expand(torch.from_numpy(ids[10:20]).cuda(), cu, torch.from_numpy(cu).cuda(), kpool,
+                       budget, 10, 20).cpu().numpy()
+        np.testing.assert_array_equal(sub, got[10:20])
