@@ -1,0 +1,245 @@
+"""Benchmark of the k-pool indexer selection on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload sq524288] [--no-cpu-baseline]
+
+One step is the whole path (pool the keys, score + select every row through
+the 2 GiB chunk loop, expand to token ids) over the workload's rows, on
+synthetic seeded inputs already resident in HBM.  Prints ONE JSON line:
+
+  value       visible (row, pool) scores per second of whole-path wall time
+  ms_per_step selection wall time of one step
+  roofline    the score kernel (the dominant kernel): algorithmic MFMA flops
+              (2*H*D per visible pair) over its average launch time, measured
+              with HIP events on the launch stream inside the timed region,
+              against the 2.5 PFLOP/s dense bf16 peak
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same
+              workload's rows, extrapolated to the whole job by visible pairs
+
+The pages' own figure for this workload (KPool selection at 512k tokens on
+one B200, 21.07 s) is reported as context only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+PAGES_B200_SELECTION_S = {"sq524288": 21.07, "sq524288_slice": 2.63}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(cu, q_lo, q_hi, kpool):
+    """Number of (row, pool) pairs with p*kpool <= t over rows [q_lo, q_hi)."""
+    tot = 0
+    for s in range(len(cu) - 1):
+        a, b = max(q_lo, int(cu[s])), min(q_hi, int(cu[s + 1]))
+        if a >= b:
+            continue
+        t0, t1 = a - int(cu[s]), b - int(cu[s])          # local positions [t0, t1)
+        t = np.arange(t0, t1, dtype=np.int64)
+        tot += int((t // kpool + 1).sum())
+    return tot
+
+
+def cpu_baseline(wl, inp, total_pairs, seed, budget_s=15.0):
+    """Oracle on sampled rows of the same workload; rate extrapolated by visible pairs.
+
+    The oracle reads the same seeded inputs (copied back from the device
+    tensors the generator filled) and runs pool -> score -> select -> expand
+    for each sampled row, as it stands.
+    """
+    import torch
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 0) for d in threadpool_info()] or [cores])
+    except Exception:
+        threads = cores
+    cu = np.asarray(inp["cu_seqlens"])
+    lo, hi = wl.rows
+    k = inp["k"].cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    kp = oracle.pool_keys(k, cu, wl.kpool)
+    t_pool = time.perf_counter() - t0
+    cu_pools, _ = oracle.count_pools(cu, wl.kpool)
+    # 64 evenly spaced rows (always the first and last), then random rows until the time budget
+    first = np.unique(np.linspace(lo, hi - 1, 64).astype(np.int64))
+    extra = np.random.default_rng(seed).permutation(np.arange(lo, hi))[:8192]
+    batches = [first] + [np.sort(extra[i:i + 32]) for i in range(0, len(extra), 32)]
+    sample_pairs = nrows = 0
+    t_rows = 0.0
+    for batch in batches:
+        idx = torch.from_numpy(batch).to(inp["q"].device)
+        qs = inp["q"].index_select(0, idx).cpu().numpy().view(np.uint16)
+        ws = inp["w"].index_select(0, idx).cpu().numpy()
+        t1 = time.perf_counter()
+        seq, t = oracle.row_positions(batch, cu)
+        for i in range(len(batch)):
+            sc = oracle.row_scores(qs[i:i + 1], ws[i:i + 1], kp, cu_pools, seq[i:i + 1], t[i:i + 1],
+                                   wl.kpool)
+            n = int(t[i] // wl.kpool + 1)
+            ids = oracle.select_row(sc[0, :n], wl.budget)
+            oracle.expand_row(ids, int(t[i]), wl.kpool)
+            sample_pairs += n
+        t_rows += time.perf_counter() - t1
+        nrows += len(batch)
+        if t_rows + t_pool >= budget_s:
+            break
+    est_full_s = t_pool + t_rows * (total_pairs / max(sample_pairs, 1))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": total_pairs / est_full_s,
+        "unit": "scores/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{nrows} rows of {wl.name} (64 evenly spaced incl. first and last, then random), "
+                   f"{sample_pairs} visible pairs scored, selected and expanded in {t_rows:.1f} s, "
+                   f"plus pooling all {wl.T} keys in {t_pool:.1f} s; whole-job time extrapolated "
+                   f"by visible pairs = {est_full_s:.0f} s; host {cpu_model or platform.processor()}, "
+                   f"{cores} cores visible, BLAS threads {threads}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="sq524288")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the selection would "
+              "shard by query rows with one int32 all-gather; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from pool_score_top_amd import kpool as K
+    from pool_score_top_amd import synth
+
+    wl = synth.workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {wl.name} inputs (T={wl.T}, H={wl.H}, D={wl.D})")
+    t0 = time.time()
+    inp = synth.device_inputs(wl, args.seed, device=dev)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    cu = inp["cu_seqlens"]
+    q_lo, q_hi = wl.rows
+    sel = K.Selector(cu, wl.kpool, wl.budget, wl.H, wl.D, device=dev, q_lo=q_lo, q_hi=q_hi)
+    pairs = visible_pairs(cu, q_lo, q_hi, wl.kpool)
+    flops = 2.0 * wl.H * wl.D * pairs
+
+    for i in range(args.warmup):
+        sel.run(inp["q"], inp["k"], inp["w"])
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i} done")
+
+    K.profile_enable(True)
+    K.profile_collect()  # reset
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sel.run(inp["q"], inp["k"], inp["w"])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = K.profile_collect()
+    K.profile_enable(False)
+    ms_step = 1000.0 * elapsed / args.steps
+    log(f"[bench] {args.steps} steps, {ms_step:.2f} ms/step")
+
+    score_ms, score_n = prof["score"]
+    topk_ms, topk_n = prof["topk"]
+    pool_ms, _ = prof["pool_keys"]
+    exp_ms, _ = prof["expand"]
+    S = args.steps
+    rows = q_hi - q_lo
+    score_tflops = flops * S / (score_ms / 1000.0) / 1e12
+    topk_bytes = 4.0 * pairs + 4.0 * wl.budget * rows
+    topk_gbs = topk_bytes * S / (topk_ms / 1000.0) / 1e9
+    exp_bytes = 4.0 * wl.budget * rows * (1 + wl.kpool)
+    exp_gbs = exp_bytes * S / (exp_ms / 1000.0) / 1e9 if exp_ms > 0 else 0.0
+    pool_bytes = 2.0 * wl.T * wl.D + 2.0 * sel.P_tot * wl.D
+    pool_gbs = pool_bytes * S / (pool_ms / 1000.0) / 1e9 if pool_ms > 0 else 0.0
+
+    result = {
+        "metric": "query-pool scores/s + selection wall time at 512k tokens, % MFMA/HBM peak",
+        "value": pairs / (ms_step / 1000.0),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: {len(cu) - 1} sequence(s), {wl.T} tokens, rows [{q_lo}, {q_hi}), "
+                         f"H={wl.H}, D={wl.D}, kpool={wl.kpool}, budget={wl.budget} pools, causal"),
+            "tokens": wl.T, "rows": rows, "H": wl.H, "D": wl.D, "kpool": wl.kpool,
+            "budget": wl.budget, "visible_pairs": pairs, "seed": args.seed,
+            "score_chunk_rows": int(sel.workspace.numel() // (((sel.max_pools + 63) // 64) * 64 * 4)),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "score_kernel<32,128>",
+            "achieved": score_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": score_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "launches_per_step": score_n // S,
+            "flops_per_launch": flops / max(1, score_n // S),
+            "avg_launch_ms": score_ms / max(1, score_n),
+        },
+        "kernels": {
+            "score": {"ms_per_step": score_ms / S, "tflops": score_tflops,
+                      "mfma_frac": score_tflops / PEAK_BF16_TFLOPS},
+            "topk": {"ms_per_step": topk_ms / S, "gbs_algorithmic": topk_gbs,
+                     "hbm_frac": topk_gbs / PEAK_HBM_GBS, "launches_per_step": topk_n // S},
+            "pool_keys": {"ms_per_step": pool_ms / S, "gbs": pool_gbs},
+            "expand": {"ms_per_step": exp_ms / S, "gbs": exp_gbs},
+        },
+        "pages_context": {
+            "b200_selection_s": PAGES_B200_SELECTION_S.get(wl.name),
+            "ratio_b200_time_over_ours": (PAGES_B200_SELECTION_S[wl.name] / (ms_step / 1000.0)
+                                          if wl.name in PAGES_B200_SELECTION_S else None),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of the same workload")
+        result["cpu_baseline"] = cpu_baseline(wl, inp, pairs, args.seed, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
