@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   const uint16_t *kps = kp + (int64_t)segs.pool_base[g] * D;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
   const int lg = lane >> 4;  // lane group: K slice of the operands, head quad of the output
   const int lc = lane & 15;  // operand row (head) / output column (pool)
   const int wr0 = wave * kRowsPerWave;
@@ -118,7 +118,8 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // visible pools of the row this lane stores (row wr0 + lg), and of the wave's last row
   const int my_nvis = (wr0 + lg < nrows) ? (int)((t0 + wr0 + lg) / kpool) + 1 : 0;
   const int wave_last = min(nrows, wr0 + kRowsPerWave) - 1;
-  const int wave_nvis = (wave_last >= wr0) ? (int)((t0 + wave_last) / kpool) + 1 : 0;
+  const int wave_nvis = __builtin_amdgcn_readfirstlane(
+      (wave_last >= wr0) ? (int)((t0 + wave_last) / kpool) + 1 : 0);
   float *orow = out + (row0 + wr0 + lg - chunk_row0) * ld;
 
   // ---- pooled-key stages through LDS ---------------------------------------
@@ -156,28 +157,39 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     const int stage_base = p_begin + st * kStagePools;
     if (st + 1 < nstage) fetch(stage_base + kStagePools);
     const unsigned char *sb = lds + (st & 1) * S::STAGE_BYTES;
+    // 16-pool sub-tiles of this stage that hold pools visible to this wave's rows
+    const int lim = min(wave_nvis, p_end) - stage_base;
+    const int nsub = __builtin_amdgcn_readfirstlane(
+        lim <= 0 ? 0 : min(kStagePools / kSub, (lim + kSub - 1) / kSub));
 #pragma unroll 1
-    for (int sub = 0; sub < kStagePools / kSub; ++sub) {
+    for (int sub = 0; sub < nsub; ++sub) {
       const int pbase = stage_base + sub * kSub;
-      if (pbase >= wave_nvis || pbase >= p_end) break;  // wave-uniform
       bf16x8 b[S::KS];
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks)
         b[ks] = *reinterpret_cast<const bf16x8 *>(sb + (sub * kSub + lc) * S::PITCH +
                                                   (lg * S::KG + ks * 8) * 2);
+      // all (row, M block) accumulators advance together: 8 independent MFMAs per K step
+      floatx4 acc[kRowsPerWave][S::MB];
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+        for (int mb = 0; mb < S::MB; ++mb) acc[r][mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks)
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+          for (int mb = 0; mb < S::MB; ++mb)
+            acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], acc[r][mb], 0, 0, 0);
       float x[kRowsPerWave];
 #pragma unroll
       for (int r = 0; r < kRowsPerWave; ++r) {
         x[r] = 0.0f;
 #pragma unroll
-        for (int mb = 0; mb < S::MB; ++mb) {
-          floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int mb = 0; mb < S::MB; ++mb)
 #pragma unroll
-          for (int ks = 0; ks < S::KS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], acc, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(acc[i], 0.0f), sw[r][mb][i], x[r]);
-        }
+          for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(acc[r][mb][i], 0.0f), sw[r][mb][i], x[r]);
       }
       // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
       const float y01 = swap16_sum(x[0], x[1]);
