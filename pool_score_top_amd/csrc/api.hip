@@ -38,7 +38,10 @@ int ok() {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t kChunkCapBytes = int64_t(1) << 31;  // 2 GiB of fp32 scores per chunk
-constexpr int kPoolSegMax = 2048;                     // pools per score workgroup (max)
+#ifndef KPOOL_POOL_SEG_MAX
+#define KPOOL_POOL_SEG_MAX 4096
+#endif
+constexpr int kPoolSegMax = KPOOL_POOL_SEG_MAX;  // pools per score workgroup (max, multiple of 64)
 
 int64_t pitch_of(int32_t max_pools) { return (int64_t)(max_pools + 63) / 64 * 64; }
 

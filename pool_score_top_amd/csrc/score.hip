@@ -50,10 +50,11 @@ struct Shape {
   static constexpr int DP = (D + 31) / 32 * 32;   // head dim padded to the K step
   static constexpr int KS = DP / 32;              // K steps per dot product
   static constexpr int KG = DP / 4;               // contiguous dims per lane group
-  static constexpr int PITCH = DP * 2 + 16;       // LDS bytes per pooled key (+16: bank skew)
-  static constexpr int STAGE_BYTES = kStagePools * PITCH;
-  static constexpr int CHUNKS = kStagePools * DP / 8;  // 16-byte pieces per stage
-  static constexpr int CPT = (CHUNKS + kWaves * 64 - 1) / (kWaves * 64);  // pieces per thread
+  static constexpr int ROWB = DP * 2;             // LDS bytes per pooled key (no padding)
+  static constexpr int NSLOT = DP / 8;            // 16-byte slots per key row
+  static constexpr int STAGE_BYTES = kStagePools * ROWB;
+  static constexpr int NREG = STAGE_BYTES / 1024; // 1 KiB DMA regions per stage (one per wave op)
+  static constexpr int RPW = (NREG + kWaves - 1) / kWaves;  // regions per wave
 };
 
 // permlane16_swap(a, b) gives a' = [a.g0, b.g0, a.g2, b.g2] and b' = [a.g1, b.g1, a.g3, b.g3]
@@ -91,118 +92,152 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   const int wr0 = wave * kRowsPerWave;
 
   // ---- per-row operands, resident for the whole kernel --------------------
+  // Loads are unconditional from clamped, in-bounds addresses (the tile's last row,
+  // the last head / dim slice), and masked lanes are zeroed afterwards, so the
+  // compiler issues all of them back to back with no branch or wait in between.
   bf16x8 a[kRowsPerWave][S::MB][S::KS];
   float sw[kRowsPerWave][S::MB][4];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     const bool valid = wr0 + r < nrows;
-    const int64_t grow = row0 + wr0 + r;
+    const int64_t grow = row0 + min(wr0 + r, nrows - 1);
 #pragma unroll
     for (int mb = 0; mb < S::MB; ++mb) {
       const int head = mb * 16 + lc;
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
         const int kk = lg * S::KG + ks * 8;
-        bf16x8 v = {};
-        if (valid && head < H && kk < D)
-          v = *reinterpret_cast<const bf16x8 *>(q + (grow * H + head) * D + kk);
-        a[r][mb][ks] = v;
+        const bool ok = valid && head < H && kk < D;
+        const uint4 v = *reinterpret_cast<const uint4 *>(q + (grow * H + min(head, H - 1)) * D +
+                                                         min(kk, D - 8));
+        const uint4 z = ok ? v : make_uint4(0, 0, 0, 0);
+        a[r][mb][ks] = __builtin_bit_cast(bf16x8, z);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = mb * 16 + lg * 4 + i;
-        sw[r][mb][i] = (valid && h < H) ? scale * w[grow * H + h] : 0.0f;
-      }
+      const int h0 = mb * 16 + lg * 4;  // this lane's 4 output heads; H % 4 == 0
+      const float4 wv = *reinterpret_cast<const float4 *>(w + grow * H + min(h0, H - 4));
+      const bool wok = valid && h0 < H;
+      sw[r][mb][0] = wok ? scale * wv.x : 0.0f;
+      sw[r][mb][1] = wok ? scale * wv.y : 0.0f;
+      sw[r][mb][2] = wok ? scale * wv.z : 0.0f;
+      sw[r][mb][3] = wok ? scale * wv.w : 0.0f;
     }
   }
-  // visible pools of the row this lane stores (row wr0 + lg), and of the wave's last row
+  // visible pools of the row this lane stores (row wr0 + lg)
   const int my_nvis = (wr0 + lg < nrows) ? (int)((t0 + wr0 + lg) / kpool) + 1 : 0;
-  const int wave_last = min(nrows, wr0 + kRowsPerWave) - 1;
-  const int wave_nvis = __builtin_amdgcn_readfirstlane(
-      (wave_last >= wr0) ? (int)((t0 + wave_last) / kpool) + 1 : 0);
-  float *orow = out + (row0 + wr0 + lg - chunk_row0) * ld;
+  float *orow = out + (row0 + min(wr0 + lg, nrows - 1) - chunk_row0) * ld;
 
   // ---- pooled-key stages through LDS ---------------------------------------
-  uint4 pre[S::CPT];
-  auto fetch = [&](int stage_base) {
+  // Keys go global -> LDS with direct DMA loads (global_load_lds_dwordx4): one wave
+  // instruction fills one contiguous 1 KiB region, lane i writing bytes [16i, 16i+16).
+  // Within a key row, 16-byte slot j holds chunk j ^ (pool mod NSLOT) of the key, an XOR
+  // swizzle that keeps the B-fragment reads of 16 consecutive pools on distinct banks.
+  // Loads are clamped and unconditional: pools past p_end are never stored, and chunks
+  // past D (padding of the K step) meet zero q fragments, so duplicates are harmless.
+  int dma_pool[S::RPW], dma_off[S::RPW];
 #pragma unroll
-    for (int c = 0; c < S::CPT; ++c) {
-      const int piece = threadIdx.x + c * kWaves * 64;
-      const int pl = piece / (S::DP / 8);
-      const int part = piece - pl * (S::DP / 8);
-      const int pool = stage_base + pl;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (piece < S::CHUNKS && pool < p_end && part * 8 < D)
-        v = *reinterpret_cast<const uint4 *>(kps + (int64_t)pool * D + part * 8);
-      pre[c] = v;
+  for (int i = 0; i < S::RPW; ++i) {
+    const int region = min(wave + i * kWaves, S::NREG - 1);
+    const int byte = region * 1024 + lane * 16;
+    dma_pool[i] = byte / S::ROWB;
+    const int slot = (byte % S::ROWB) / 16;
+    dma_off[i] = min((slot ^ (dma_pool[i] % S::NSLOT)) * 8, D - 8);
+  }
+  auto dma_stage = [&](int stage_base, int buf) {
+#pragma unroll
+    for (int i = 0; i < S::RPW; ++i) {
+      if (wave + i * kWaves < S::NREG) {  // wave-uniform
+        const int pool = min(stage_base + dma_pool[i], p_end - 1);
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
+        __builtin_amdgcn_global_load_lds(
+            kps + (int64_t)pool * D + dma_off[i],
+            (__attribute__((address_space(3))) void *)(lds + buf * S::STAGE_BYTES +
+                                                       (wave + i * kWaves) * 1024),
+            16, 0, 0);
+#else
+        (void)pool;
+#endif
+      }
     }
   };
-  auto stash = [&](int buf) {
+  // B fragment of (pool row `pl` of a stage, chunk `c`) under the swizzle
+  auto b_addr = [&](int pl, int c) { return pl * S::ROWB + ((c ^ (pl % S::NSLOT)) * 16); };
+
+  // One stage's scores stay in registers (one value per lane per 16-pool sub-tile) and
+  // are stored after the stage's barrier: stores are then issued before the next
+  // stage's key fetch, so waiting for that fetch never waits on fresh stores.
+  constexpr int kSubs = kStagePools / kSub;
+  // Every stage computes all its sub-tiles (no branches between the LDS prefetches and
+  // the MFMAs); only pools visible to the lane's row and inside this workgroup's pool
+  // segment are stored, so columns of neighbouring segments are never touched.
+  const int store_lim = min(my_nvis, p_end);
+  float vals[kSubs];
+  int st_base = -(1 << 30);  // the stage whose scores are pending in vals (none yet)
+  auto flush = [&]() {
 #pragma unroll
-    for (int c = 0; c < S::CPT; ++c) {
-      const int piece = threadIdx.x + c * kWaves * 64;
-      if (piece < S::CHUNKS) {
-        const int pl = piece / (S::DP / 8);
-        const int part = piece - pl * (S::DP / 8);
-        *reinterpret_cast<uint4 *>(lds + buf * S::STAGE_BYTES + pl * S::PITCH + part * 16) = pre[c];
-      }
+    for (int sub = 0; sub < kSubs; ++sub) {
+      const int p = st_base + sub * kSub + lc;
+      if (p >= 0 && p < store_lim) orow[p] = vals[sub];
     }
   };
 
   const int nstage = (p_end - p_begin + kStagePools - 1) / kStagePools;
-  fetch(p_begin);
-  stash(0);
+  dma_stage(p_begin, 0);
   __syncthreads();
   for (int st = 0; st < nstage; ++st) {
     const int stage_base = p_begin + st * kStagePools;
-    if (st + 1 < nstage) fetch(stage_base + kStagePools);
+    flush();
+    if (st + 1 < nstage) dma_stage(stage_base + kStagePools, (st + 1) & 1);
     const unsigned char *sb = lds + (st & 1) * S::STAGE_BYTES;
-    // 16-pool sub-tiles of this stage that hold pools visible to this wave's rows
-    const int lim = min(wave_nvis, p_end) - stage_base;
-    const int nsub = __builtin_amdgcn_readfirstlane(
-        lim <= 0 ? 0 : min(kStagePools / kSub, (lim + kSub - 1) / kSub));
-#pragma unroll 1
-    for (int sub = 0; sub < nsub; ++sub) {
-      const int pbase = stage_base + sub * kSub;
-      bf16x8 b[S::KS];
+    // B fragments are read one sub-tile ahead (unconditionally: reading a sub-tile this
+    // wave then skips is harmless), so LDS latency hides behind the current MFMAs.
+    bf16x8 bb[2][S::KS];
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks)
-        b[ks] = *reinterpret_cast<const bf16x8 *>(sb + (sub * kSub + lc) * S::PITCH +
-                                                  (lg * S::KG + ks * 8) * 2);
-      // all (row, M block) accumulators advance together: 8 independent MFMAs per K step
-      floatx4 acc[kRowsPerWave][S::MB];
+    for (int ks = 0; ks < S::KS; ++ks)
+      bb[0][ks] = *reinterpret_cast<const bf16x8 *>(sb + b_addr(lc, lg * (S::KG / 8) + ks));
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r)
+    for (int sub = 0; sub < kSubs; ++sub) {
+      if (sub + 1 < kSubs) {
 #pragma unroll
-        for (int mb = 0; mb < S::MB; ++mb) acc[r][mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks)
+        for (int ks = 0; ks < S::KS; ++ks)
+          bb[(sub + 1) & 1][ks] = *reinterpret_cast<const bf16x8 *>(
+              sb + b_addr((sub + 1) * kSub + lc, lg * (S::KG / 8) + ks));
+      }
+      {
+        const bf16x8 (&b)[S::KS] = bb[sub & 1];
+        // all (row, M block) accumulators advance together: 8 independent MFMAs per K step
+        floatx4 acc[kRowsPerWave][S::MB];
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r)
 #pragma unroll
+          for (int mb = 0; mb < S::MB; ++mb) acc[r][mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks)
+#pragma unroll
+          for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+            for (int mb = 0; mb < S::MB; ++mb)
+              acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], acc[r][mb], 0, 0, 0);
+        float x[kRowsPerWave];
+#pragma unroll
+        for (int r = 0; r < kRowsPerWave; ++r) {
+          x[r] = 0.0f;
+#pragma unroll
           for (int mb = 0; mb < S::MB; ++mb)
-            acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], acc[r][mb], 0, 0, 0);
-      float x[kRowsPerWave];
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) {
-        x[r] = 0.0f;
-#pragma unroll
-        for (int mb = 0; mb < S::MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(acc[r][mb][i], 0.0f), sw[r][mb][i], x[r]);
+            for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(acc[r][mb][i], 0.0f), sw[r][mb][i], x[r]);
+        }
+        // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
+        const float y01 = swap16_sum(x[0], x[1]);
+        const float y23 = swap16_sum(x[2], x[3]);
+        // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
+        auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
+        vals[sub] = __uint_as_float(z[0]) + __uint_as_float(z[1]);
       }
-      // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
-      const float y01 = swap16_sum(x[0], x[1]);
-      const float y23 = swap16_sum(x[2], x[3]);
-      // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
-      auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
-      const float val = __uint_as_float(z[0]) + __uint_as_float(z[1]);
-      const int p = pbase + lc;
-      if (p < my_nvis) orow[p] = val;
     }
-    if (st + 1 < nstage) stash((st + 1) & 1);
-    __syncthreads();
+    st_base = stage_base;
+    __syncthreads();  // also waits for this wave's DMA of the next stage
   }
+  flush();
 }
 
 template <int H, int D>
