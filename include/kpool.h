@@ -80,10 +80,11 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host,
                     const int32_t *cu_seqlens_dev, const int32_t *cu_pools_dev,
                     int32_t nseq, int32_t D, int32_t kpool, uint16_t *kp, void *stream);
 
-/* Workspace for kpool_score_topk over rows [q_lo, q_hi): one fp32 score row
- * per query row, at a row pitch of max_pools rounded up to 64, capped at
- * 2 GiB per chunk (Megatron-LM PR #8299 "Change": the chunked score path
- * caps its score buffer at 2 GiB).  Returns 0 for an empty range. */
+/* Workspace for kpool_score_topk over rows [q_lo, q_hi): per query row of a
+ * chunk, one fp32 score row at a pitch of max_pools rounded up to 64 plus one
+ * fp32 maximum per 16 pools of it; the score rows of a chunk are capped at
+ * 2 GiB (Megatron-LM PR #8299 "Change": the chunked score path caps its score
+ * buffer at 2 GiB).  Returns 0 for an empty range. */
 size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools);
 
 /* Step 2 - score and select, for the global rows [q_lo, q_hi).
@@ -95,9 +96,10 @@ size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools);
  *   w        fp32 [T, H]       per-row head weights (any sign)
  *   scale    > 0, usually 1/sqrt(D)
  *   budget   pools kept per row, 1..1024 (index_topk / kpool)
- *   workspace, workspace_bytes: device scratch of at least one score row
+ *   workspace, workspace_bytes: device scratch of at least one row
  *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools)); rows are
- *            processed in chunks of min(2 GiB, workspace_bytes) / pitch.
+ *            processed in chunks of as many rows as both the 2 GiB score cap
+ *            and the workspace allow.  Contents are scratch on return.
  *   pool_ids int32 [q_hi - q_lo, budget] output: sequence-local pool ids,
  *            best first by (score desc, pool asc), -1 after the visible pools
  *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.

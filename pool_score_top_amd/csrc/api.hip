@@ -135,11 +135,14 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host, const int
   return ok();
 }
 
+// Per row of a chunk the workspace holds ld fp32 scores and ld/16 fp32 group maxima.
+int64_t ws_row_bytes(int64_t ld) { return (ld + ld / kpool::kGroup) * 4; }
+
 size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools) {
   if (q_hi <= q_lo || max_pools <= 0) return 0;
-  const int64_t row_bytes = pitch_of(max_pools) * 4;
-  const int64_t cap_rows = std::max<int64_t>(1, kChunkCapBytes / row_bytes);
-  return (size_t)(std::min<int64_t>(q_hi - q_lo, cap_rows) * row_bytes);
+  const int64_t ld = pitch_of(max_pools);
+  const int64_t cap_rows = std::max<int64_t>(1, kChunkCapBytes / (ld * 4));
+  return (size_t)(std::min<int64_t>(q_hi - q_lo, cap_rows) * ws_row_bytes(ld));
 }
 
 int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
@@ -169,14 +172,17 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
   int32_t max_pools = 0;
   kpool_count_pools(cu_seqlens_host, nseq, kpool, cu_pools.data(), &max_pools);
   const int64_t ld = pitch_of(max_pools);
-  const int64_t row_bytes = ld * 4;
+  const int64_t ldg = ld / kpool::kGroup;
+  const int64_t row_bytes = ws_row_bytes(ld);
   if (!workspace || (int64_t)workspace_bytes < row_bytes)
     return fail(KPOOL_EWORKSPACE, "%s: workspace must hold one score row (%lld bytes), got %zu", fn,
                 (long long)row_bytes, workspace_bytes);
   if (!aligned16(workspace)) return fail(KPOOL_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-  const int64_t chunk_rows =
-      std::max<int64_t>(1, std::min<int64_t>(kChunkCapBytes, (int64_t)workspace_bytes) / row_bytes);
+  // rows per chunk: the fp32 score buffer stays within 2 GiB and the workspace
+  const int64_t chunk_rows = std::max<int64_t>(
+      1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / row_bytes));
   float *ws = (float *)workspace;
+  float *gws = ws + chunk_rows * ld;  // group maxima follow the score rows
   hipStream_t st = (hipStream_t)stream;
   const int tile_rows = kpool::score_tile_rows();
 
@@ -214,13 +220,13 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
       const int32_t npseg = (int32_t)((max_npv + pseg - 1) / pseg);
       hipError_t e = timed(1, st, [&] {
         return kpool::launch_score(H, D, q, kp, w, scale, kpool, L, ntiles, npseg, (int32_t)pseg,
-                                   c0, ld, ws, st);
+                                   c0, ld, ws, ldg, gws, st);
       });
       if (e != hipSuccess) return hip_fail(fn, e);
     }
     hipError_t e = timed(2, st, [&] {
       return kpool::launch_topk(ws, ld, c1 - c0, nullptr, cu_seqlens_dev, nseq, c0, kpool, budget,
-                                pool_ids + (c0 - q_lo) * budget, st);
+                                pool_ids + (c0 - q_lo) * budget, gws, ldg, st);
     });
     if (e != hipSuccess) return hip_fail(fn, e);
     if (scores_out) {
@@ -270,7 +276,8 @@ int kpool_topk(const float *scores, int64_t ld, const int32_t *n_valid, int64_t 
   if (rows > 0x7FFFFFFF) return fail(KPOOL_EINVAL, "%s: too many rows", fn);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(2, st, [&] {
-    return kpool::launch_topk(scores, ld, rows, n_valid, nullptr, 0, 0, 1, budget, pool_ids, st);
+    return kpool::launch_topk(scores, ld, rows, n_valid, nullptr, 0, 0, 1, budget, pool_ids,
+                              nullptr, 0, st);
   });
   if (e != hipSuccess) return hip_fail(fn, e);
   return ok();

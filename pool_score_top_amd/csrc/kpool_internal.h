@@ -35,19 +35,26 @@ hipError_t launch_pool_keys(const uint16_t *k, const int32_t *cu_seqlens, const 
 // true if (H, D) has a compiled score kernel
 bool score_supported(int H, int D);
 int score_tile_rows();
+// Scores of the chunk's rows go to out[(row - chunk_row0) * ld + pool]; the max of each
+// 16-pool group of a row (over its visible pools) to gmax[(row - chunk_row0) * ldg + pool/16].
+constexpr int kGroup = 16;
 hipError_t launch_score(int H, int D, const uint16_t *q, const uint16_t *kp, const float *w,
                         float scale, int32_t kpool, const SegList &segs, int32_t ntiles,
                         int32_t npseg, int32_t pseg_pools, int64_t chunk_row0, int64_t ld,
-                        float *out, hipStream_t stream);
+                        float *out, int64_t ldg, float *gmax, hipStream_t stream);
 
 constexpr int kTopkMaxBudget = 1024;
 // Rows [row0, row0 + nrows) of `scores` (row r at scores + r*ld).  The number
 // of ranked entries of row r is n_valid[r] if n_valid is not null, else
 // (t / kpool + 1) for the row's sequence-local position t (global row
 // grow0 + r looked up in cu_seqlens).
+// With gmax (the score kernel's 16-pool group maxima, row pitch ldg) the selection reads
+// the group maxima first and then only the groups that can hold a winner; without it
+// every row is read in full.
 hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
                        const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
-                       int32_t budget, int32_t *out, hipStream_t stream);
+                       int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
+                       hipStream_t stream);
 
 hipError_t launch_scores_copy(const float *ws, int64_t ld, int64_t nrows, const int32_t *cu_seqlens,
                               int32_t nseq, int64_t grow0, int32_t kpool, float *dst,

@@ -64,11 +64,20 @@ __device__ inline float swap16_sum(float a, float b) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Max over each 16-lane row, in every lane: quad swaps, then half-row and row mirrors (DPP).
+__device__ inline float max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
+  return v;
+}
+
 template <int H, int D>
 __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kp, const float *__restrict__ w,
     float scale, int kpool, SegList segs, int npseg, int pseg_pools, int64_t chunk_row0,
-    int64_t ld, float *__restrict__ out) {
+    int64_t ld, float *__restrict__ out, int64_t ldg, float *__restrict__ gmax) {
   using S = Shape<H, D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
@@ -125,6 +134,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // visible pools of the row this lane stores (row wr0 + lg)
   const int my_nvis = (wr0 + lg < nrows) ? (int)((t0 + wr0 + lg) / kpool) + 1 : 0;
   float *orow = out + (row0 + min(wr0 + lg, nrows - 1) - chunk_row0) * ld;
+  float *grow_max = gmax + (row0 + min(wr0 + lg, nrows - 1) - chunk_row0) * ldg;
 
   // ---- pooled-key stages through LDS ---------------------------------------
   // Keys go global -> LDS with direct DMA loads (global_load_lds_dwordx4): one wave
@@ -169,14 +179,19 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // Every stage computes all its sub-tiles (no branches between the LDS prefetches and
   // the MFMAs); only pools visible to the lane's row and inside this workgroup's pool
   // segment are stored, so columns of neighbouring segments are never touched.
+  // Alongside the scores, the max of every 16-pool group of a row (over its visible
+  // pools) goes to `gmax`; the selection reads those first and then only the groups
+  // that can hold a winner.
   const int store_lim = min(my_nvis, p_end);
-  float vals[kSubs];
+  float vals[kSubs], gvals[kSubs];
   int st_base = -(1 << 30);  // the stage whose scores are pending in vals (none yet)
   auto flush = [&]() {
 #pragma unroll
     for (int sub = 0; sub < kSubs; ++sub) {
       const int p = st_base + sub * kSub + lc;
       if (p >= 0 && p < store_lim) orow[p] = vals[sub];
+      const int g0 = st_base + sub * kSub;
+      if (lc == 0 && g0 >= 0 && g0 < store_lim) grow_max[g0 / kSub] = gvals[sub];
     }
   };
 
@@ -231,7 +246,9 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
         const float y23 = swap16_sum(x[2], x[3]);
         // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
         auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
-        vals[sub] = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+        const float v = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+        vals[sub] = v;
+        gvals[sub] = max16(stage_base + sub * kSub + lc < my_nvis ? v : -__builtin_inff());
       }
     }
     st_base = stage_base;
@@ -244,12 +261,12 @@ template <int H, int D>
 hipError_t launch_t(const uint16_t *q, const uint16_t *kp, const float *w, float scale,
                     int32_t kpool, const SegList &segs, int32_t ntiles, int32_t npseg,
                     int32_t pseg_pools, int64_t chunk_row0, int64_t ld, float *out,
-                    hipStream_t stream) {
+                    int64_t ldg, float *gmax, hipStream_t stream) {
   using S = Shape<H, D>;
   const size_t lds = 2 * S::STAGE_BYTES;
   const unsigned grid = (unsigned)ntiles * (unsigned)npseg;
   hipLaunchKernelGGL((score_kernel<H, D>), dim3(grid), dim3(kWaves * 64), lds, stream, q, kp, w,
-                     scale, kpool, segs, npseg, pseg_pools, chunk_row0, ld, out);
+                     scale, kpool, segs, npseg, pseg_pools, chunk_row0, ld, out, ldg, gmax);
   return hipGetLastError();
 }
 
@@ -261,14 +278,14 @@ int score_tile_rows() { return kTileRows; }
 hipError_t launch_score(int H, int D, const uint16_t *q, const uint16_t *kp, const float *w,
                         float scale, int32_t kpool, const SegList &segs, int32_t ntiles,
                         int32_t npseg, int32_t pseg_pools, int64_t chunk_row0, int64_t ld,
-                        float *out, hipStream_t stream) {
+                        float *out, int64_t ldg, float *gmax, hipStream_t stream) {
   if (pseg_pools % kStagePools != 0) return hipErrorInvalidValue;
   if (H == 32 && D == 128)
     return launch_t<32, 128>(q, kp, w, scale, kpool, segs, ntiles, npseg, pseg_pools, chunk_row0,
-                             ld, out, stream);
+                             ld, out, ldg, gmax, stream);
   if (H == 4 && D == 16)
     return launch_t<4, 16>(q, kp, w, scale, kpool, segs, ntiles, npseg, pseg_pools, chunk_row0,
-                           ld, out, stream);
+                           ld, out, ldg, gmax, stream);
   return hipErrorInvalidValue;
 }
 

@@ -124,22 +124,47 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
   }
 }
 
+constexpr int kGroupCap = 4096;  // candidate 16-pool groups held in LDS
+
 struct Smem {
   uint64_t cand[kCandCap];
+  uint32_t glist[kGroupCap];
   uint32_t hist[256];
   uint32_t wave_bound[kWavesT];
   uint64_t prefix;
   uint32_t count;
+  uint32_t gcount;
   int32_t pbits;
   int32_t krem;
   int32_t done;
 };
 
+// Wave-aggregated append: lanes with c (0..4) items reserve c consecutive slots of
+// *counter with one LDS atomic per wave; returns this lane's first slot.
+__device__ inline uint32_t wave_reserve(uint32_t c, uint32_t *counter, int lane) {
+  const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+  const uint32_t tot = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
+  if (tot == 0) return 0;
+  const uint32_t pre =
+      __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u)) +
+      2u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u)) +
+      4u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0u));
+  uint32_t base = 0;
+  if (lane == 0) base = atomicAdd(counter, tot);
+  return __shfl(base, 0) + pre;
+}
+
+// GMAX: the score kernel's per-row maxima of 16-pool groups are available (row pitch
+// ldg).  The bound then comes from the group maxima, and only the groups whose max
+// reaches it are read.
+template <bool GMAX>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                         const int32_t *__restrict__ n_valid,
                                                         const int32_t *__restrict__ cu_seqlens,
                                                         int nseq, int64_t grow0, int kpool,
-                                                        int budget, int32_t *__restrict__ out) {
+                                                        int budget, int32_t *__restrict__ out,
+                                                        const float *__restrict__ gmax,
+                                                        int64_t ldg) {
   __shared__ Smem sm;
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -154,21 +179,35 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     n = (i - cu_seqlens[s]) / kpool + 1;
   }
   const float *row = scores + r * ld;
+  const float *grow = GMAX ? gmax + r * ldg : nullptr;
+  const int64_t ng = (n + kGroup - 1) / kGroup;  // 16-pool groups of the row
+  // Group maxima are used when every thread gets at least one of them (so all 16
+  // waves contribute to the bound); shorter rows are read in full.
+  const bool use_groups = GMAX && n > budget && ng >= kThreads;
   int32_t *orow = out + r * (int64_t)budget;
-  if (tid == 0) sm.count = 0;
+  if (tid == 0) {
+    sm.count = 0;
+    sm.gcount = 0;
+  }
 
   // ---- pass 1: lower bound on the budget-th best key ----------------------
+  // Thread maxima over disjoint parts of the row (its elements, or its groups' maxima,
+  // which are elements too), so any budget of them are distinct elements.
   uint32_t bound = 0;
   if (n > budget) {
     uint32_t tmax = 0;
-    for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
-      const int64_t base = wbase + 4 * lane;
-      if (base < n) {
-        const float4 x = *reinterpret_cast<const float4 *>(row + base);
-        const float xs[4] = {x.x, x.y, x.z, x.w};
+    if (use_groups) {
+      for (int64_t g = tid; g < ng; g += kThreads) tmax = max(tmax, order_key(grow[g]));
+    } else {
+      for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
+        const int64_t base = wbase + 4 * lane;
+        if (base < n) {
+          const float4 x = *reinterpret_cast<const float4 *>(row + base);
+          const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (base + e < n) tmax = max(tmax, order_key(xs[e]));
+          for (int e = 0; e < 4; ++e)
+            if (base + e < n) tmax = max(tmax, order_key(xs[e]));
+        }
       }
     }
     const uint32_t sorted = wave_sort_desc(tmax, lane);
@@ -183,6 +222,50 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   __syncthreads();
 
   // ---- pass 2: gather candidates with key >= bound ------------------------
+  if (use_groups) {
+    // groups whose max reaches the bound (wave-uniform trip count: ng >= kThreads)
+    for (int64_t gbase = 0; gbase < ng; gbase += kThreads) {
+      const int64_t g = gbase + tid;
+      const bool sel = g < ng && order_key(grow[g]) >= bound;
+      const uint32_t pos = wave_reserve(sel ? 1u : 0u, &sm.gcount, lane);
+      if (sel && pos < (uint32_t)kGroupCap) sm.glist[pos] = (uint32_t)g;
+    }
+    __syncthreads();
+    const uint32_t gcount = sm.gcount;
+    if (gcount > (uint32_t)kGroupCap) {
+      if (tid == 0) sm.count = kCandCap + 1;  // too many groups: exact fallback below
+    } else {
+      // four threads per group, one float4 each
+      for (int64_t ibase = (int64_t)wave * 64; ibase < 4 * (int64_t)gcount; ibase += kThreads) {
+        const int64_t i = ibase + lane;
+        uint32_t keys[4] = {0, 0, 0, 0};
+        bool sel[4] = {false, false, false, false};
+        uint32_t c = 0;
+        int64_t base = 0;
+        if (i < 4 * (int64_t)gcount) {
+          base = (int64_t)sm.glist[i >> 2] * kGroup + (i & 3) * 4;
+          if (base < n) {
+            const float4 x = *reinterpret_cast<const float4 *>(row + base);
+            const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              keys[e] = order_key(xs[e]);
+              sel[e] = (base + e < n) && keys[e] >= bound;
+              c += sel[e] ? 1u : 0u;
+            }
+          }
+        }
+        uint32_t pos = wave_reserve(c, &sm.count, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (sel[e]) {
+            if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base + e));
+            ++pos;
+          }
+        }
+      }
+    }
+  } else {
   for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
     const int64_t base = wbase + 4 * lane;
     uint32_t keys[4] = {0, 0, 0, 0};
@@ -217,6 +300,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
         }
       }
     }
+  }
   }
   __syncthreads();
   uint32_t count = sm.count;
@@ -325,10 +409,15 @@ __global__ __launch_bounds__(256) void scores_copy_kernel(const float *__restric
 
 hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
                        const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
-                       int32_t budget, int32_t *out, hipStream_t stream) {
+                       int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
+                       hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)nrows), dim3(kThreads), 0, stream, scores, ld,
-                     n_valid, cu_seqlens, nseq, grow0, kpool, budget, out);
+  if (gmax)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)nrows), dim3(kThreads), 0, stream, scores,
+                       ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)nrows), dim3(kThreads), 0, stream, scores,
+                       ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
   return hipGetLastError();
 }
 

@@ -38,11 +38,12 @@ def test_library_exports_every_declared_symbol():
 def test_count_pools_and_workspace():
     cu_pools, mx, tot = K.count_pools([0, 9, 9, 37], 4)
     assert cu_pools.tolist() == [0, 3, 3, 10] and mx == 7 and tot == 10
-    # 512k tokens, kpool 4: pitch 131072 floats = 512 KiB per row -> 4096 rows per 2 GiB chunk
-    assert K.workspace_bytes(0, 524288, 131072) == 2**31
-    assert K.workspace_bytes(0, 100, 131072) == 100 * 131072 * 4
+    # 512k tokens, kpool 4: pitch 131072 floats = 512 KiB per row -> 4096 rows per 2 GiB chunk,
+    # plus one fp32 group maximum per 16 pools of each row
+    assert K.workspace_bytes(0, 524288, 131072) == 4096 * (131072 + 8192) * 4
+    assert K.workspace_bytes(0, 100, 131072) == 100 * (131072 + 8192) * 4
     assert K.workspace_bytes(5, 5, 10) == 0
-    assert K.workspace_bytes(0, 3, 1) == 3 * 64 * 4   # pitch rounds up to 64
+    assert K.workspace_bytes(0, 3, 1) == 3 * (64 + 4) * 4   # pitch rounds up to 64
 
 
 def _call_score(**kw):
@@ -73,7 +74,7 @@ def _call_score(**kw):
     (dict(q=0), K.KPOOL_EINVAL),
     (dict(q=8), K.KPOOL_EINVAL),            # misaligned
     (dict(ws=0), K.KPOOL_EWORKSPACE),
-    (dict(ws_bytes=100), K.KPOOL_EWORKSPACE),  # less than one 256-byte score row
+    (dict(ws_bytes=100), K.KPOOL_EWORKSPACE),  # less than one 272-byte workspace row
     (dict(cu=[1, 64]), K.KPOOL_EINVAL),
     (dict(cu=[0, 40, 30, 64]), K.KPOOL_EINVAL),
     (dict(nseq=0), K.KPOOL_EINVAL),

@@ -160,7 +160,8 @@ def test_row_split_and_chunking_reassemble_bitwise():
     wl, r = _inputs("sq4096", 5, T=1500)
     r["cu_seqlens"] = np.array([0, 700, 701, 1500], dtype=np.int32)
     full = run_gpu(r, wl.kpool, 64)
-    row_bytes = ((full["max_pools"] + 63) // 64) * 64 * 4
+    pitch = ((full["max_pools"] + 63) // 64) * 64
+    row_bytes = (pitch + pitch // 16) * 4     # one score row plus its 16-pool group maxima
     for bounds, cap in [((0, 333, 334, 1000, 1500), 7 * row_bytes), ((0, 1, 700, 1499, 1500), row_bytes),
                         ((0, 750, 1500), 100 * row_bytes)]:
         parts = [run_gpu(r, wl.kpool, 64, q_lo=a, q_hi=b, workspace_cap=cap)
