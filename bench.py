@@ -123,6 +123,30 @@ def cpu_baseline(wl, inp, total_pairs, seed, budget_s=15.0):
     }
 
 
+def score_traffic(workload: str):
+    """HBM bytes per score-kernel launch from the committed counter summary, or None.
+
+    The summary (profiles/score_kernel_sq524288_traffic.md) holds FETCH_SIZE and
+    WRITE_SIZE per launch, scaled by a plain-copy calibration, and the sha256 of
+    score.hip it was measured on; a changed kernel makes the figure stale (None).
+    """
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", f"score_kernel_{workload}_traffic.md")
+    src = os.path.join(ROOT, "pool_score_top_amd", "csrc", "score.hip")
+    if not os.path.exists(prof):
+        return None
+    vals = {}
+    for line in open(prof):
+        if ":" in line and line.strip().startswith("score_"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if vals.get("score_hip_sha256") != sha:
+        return None
+    return {"fetch": float(vals["score_fetch_bytes_per_launch"]),
+            "write": float(vals["score_write_bytes_per_launch"])}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,7 +156,20 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 4 times (scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 4 x 1 GiB device copies")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the selection would "
@@ -189,6 +226,7 @@ def main():
     pool_bytes = 2.0 * wl.T * wl.D + 2.0 * sel.P_tot * wl.D
     pool_gbs = pool_bytes * S / (pool_ms / 1000.0) / 1e9 if pool_ms > 0 else 0.0
 
+    traffic = score_traffic(wl.name)
     result = {
         "metric": "query-pool scores/s + selection wall time at 512k tokens, % MFMA/HBM peak",
         "value": pairs / (ms_step / 1000.0),
@@ -216,7 +254,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": score_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": (None if traffic is None else traffic["fetch"] + traffic["write"]),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_read": None if traffic is None else traffic["fetch"],
+            "traffic_write": None if traffic is None else traffic["write"],
             "launches_per_step": score_n // S,
             "flops_per_launch": flops / max(1, score_n // S),
             "avg_launch_ms": score_ms / max(1, score_n),

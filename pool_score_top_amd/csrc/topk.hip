@@ -125,6 +125,8 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
 }
 
 constexpr int kGroupCap = 4096;  // candidate 16-pool groups held in LDS
+constexpr int kRound = 8;        // group maxima loaded per thread before use
+constexpr int kPieces = 4;       // 16-byte score pieces loaded per thread before use
 
 struct Smem {
   uint64_t cand[kCandCap];
@@ -197,7 +199,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   if (n > budget) {
     uint32_t tmax = 0;
     if (use_groups) {
-      for (int64_t g = tid; g < ng; g += kThreads) tmax = max(tmax, order_key(grow[g]));
+      // rounds of kRound independent loads per thread
+      for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
+        float v[kRound];
+#pragma unroll
+        for (int j = 0; j < kRound; ++j) {
+          const int64_t g = gb + tid + (int64_t)j * kThreads;
+          v[j] = grow[min(g, ng - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < kRound; ++j)
+          if (gb + tid + (int64_t)j * kThreads < ng) tmax = max(tmax, order_key(v[j]));
+      }
     } else {
       for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
         const int64_t base = wbase + 4 * lane;
@@ -223,44 +236,57 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
 
   // ---- pass 2: gather candidates with key >= bound ------------------------
   if (use_groups) {
-    // groups whose max reaches the bound (wave-uniform trip count: ng >= kThreads)
-    for (int64_t gbase = 0; gbase < ng; gbase += kThreads) {
-      const int64_t g = gbase + tid;
-      const bool sel = g < ng && order_key(grow[g]) >= bound;
-      const uint32_t pos = wave_reserve(sel ? 1u : 0u, &sm.gcount, lane);
-      if (sel && pos < (uint32_t)kGroupCap) sm.glist[pos] = (uint32_t)g;
+    // groups whose max reaches the bound (uniform trip count; loads issued per round)
+    for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
+      float v[kRound];
+#pragma unroll
+      for (int j = 0; j < kRound; ++j) {
+        const int64_t g = gb + tid + (int64_t)j * kThreads;
+        v[j] = grow[min(g, ng - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kRound; ++j) {
+        const int64_t g = gb + tid + (int64_t)j * kThreads;
+        const bool sel = g < ng && order_key(v[j]) >= bound;
+        const uint32_t pos = wave_reserve(sel ? 1u : 0u, &sm.gcount, lane);
+        if (sel && pos < (uint32_t)kGroupCap) sm.glist[pos] = (uint32_t)g;
+      }
     }
     __syncthreads();
     const uint32_t gcount = sm.gcount;
     if (gcount > (uint32_t)kGroupCap) {
       if (tid == 0) sm.count = kCandCap + 1;  // too many groups: exact fallback below
     } else {
-      // four threads per group, one float4 each
-      for (int64_t ibase = (int64_t)wave * 64; ibase < 4 * (int64_t)gcount; ibase += kThreads) {
-        const int64_t i = ibase + lane;
-        uint32_t keys[4] = {0, 0, 0, 0};
-        bool sel[4] = {false, false, false, false};
-        uint32_t c = 0;
-        int64_t base = 0;
-        if (i < 4 * (int64_t)gcount) {
-          base = (int64_t)sm.glist[i >> 2] * kGroup + (i & 3) * 4;
-          if (base < n) {
-            const float4 x = *reinterpret_cast<const float4 *>(row + base);
-            const float xs[4] = {x.x, x.y, x.z, x.w};
+      // four threads per group, one float4 each; rounds of kPieces loads per thread
+      const int64_t npieces = 4 * (int64_t)gcount;
+      for (int64_t pb = 0; pb < npieces; pb += (int64_t)kThreads * kPieces) {
+        float4 x[kPieces];
+        int64_t base[kPieces];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              keys[e] = order_key(xs[e]);
-              sel[e] = (base + e < n) && keys[e] >= bound;
-              c += sel[e] ? 1u : 0u;
-            }
-          }
+        for (int j = 0; j < kPieces; ++j) {
+          const int64_t i = pb + tid + (int64_t)j * kThreads;
+          base[j] = i < npieces ? (int64_t)sm.glist[i >> 2] * kGroup + (i & 3) * 4 : n;
+          x[j] = *reinterpret_cast<const float4 *>(row + (base[j] < n ? base[j] : 0));
         }
-        uint32_t pos = wave_reserve(c, &sm.count, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (sel[e]) {
-            if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base + e));
-            ++pos;
+        for (int j = 0; j < kPieces; ++j) {
+          const float xs[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+          uint32_t keys[4];
+          bool sel[4];
+          uint32_t c = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            keys[e] = order_key(xs[e]);
+            sel[e] = (base[j] + e < n) && keys[e] >= bound;
+            c += sel[e] ? 1u : 0u;
+          }
+          uint32_t pos = wave_reserve(c, &sm.count, lane);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (sel[e]) {
+              if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base[j] + e));
+              ++pos;
+            }
           }
         }
       }
