@@ -1,6 +1,7 @@
 """Benchmark of the k-pool indexer selection on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload sq524288] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload sq524288] [--overlap on|off]
+                    [--no-cpu-baseline]
 
 One step is the whole path (pool the keys, score + select every row through
 the 2 GiB chunk loop, expand to token ids) over the workload's rows, on
@@ -9,9 +10,13 @@ synthetic seeded inputs already resident in HBM.  Prints ONE JSON line:
   value       visible (row, pool) scores per second of whole-path wall time
   ms_per_step selection wall time of one step
   roofline    the score kernel (the dominant kernel): algorithmic MFMA flops
-              (2*H*D per visible pair) over its average launch time, measured
-              with HIP events on the launch stream inside the timed region,
-              against the 2.5 PFLOP/s dense bf16 peak
+              (2*H*D per visible pair) over its average launch time, against
+              the 2.5 PFLOP/s dense bf16 peak.  Launch times come from HIP
+              events that the library records around each launch on its
+              stream, in a kernel pass of the same K steps run right after the
+              timed region with the chunk overlap off, so that every launch
+              runs alone (overlapped launches share the CUs and their event
+              spans include the other stream's kernels)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
               workload's rows, extrapolated to the whole job by visible pairs
 
@@ -154,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="sq524288")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--overlap", choices=("on", "off"), default="on",
+                    help="chunk overlap (two buffers on two streams) in the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -194,23 +201,37 @@ def main():
     pairs = visible_pairs(cu, q_lo, q_hi, wl.kpool)
     flops = 2.0 * wl.H * wl.D * pairs
 
+    K.set_overlap(args.overlap == "on")
     for i in range(args.warmup):
         sel.run(inp["q"], inp["k"], inp["w"])
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i} done")
 
-    K.profile_enable(True)
-    K.profile_collect()  # reset
+    # timed region: K whole steps, nothing else on the GPU
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         sel.run(inp["q"], inp["k"], inp["w"])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    ms_step = 1000.0 * elapsed / args.steps
+    log(f"[bench] {args.steps} steps, {ms_step:.2f} ms/step (overlap {args.overlap})")
+
+    # kernel pass: the same steps with every launch alone on one stream, each bracketed
+    # by HIP events on that stream
+    K.set_overlap(False)
+    K.profile_enable(True)
+    K.profile_collect()  # reset
+    torch.cuda.synchronize()
+    tk = time.perf_counter()
+    for i in range(args.steps):
+        sel.run(inp["q"], inp["k"], inp["w"])
+    torch.cuda.synchronize()
+    ms_serial = 1000.0 * (time.perf_counter() - tk) / args.steps
     prof = K.profile_collect()
     K.profile_enable(False)
-    ms_step = 1000.0 * elapsed / args.steps
-    log(f"[bench] {args.steps} steps, {ms_step:.2f} ms/step")
+    K.set_overlap(True)
+    log(f"[bench] kernel pass: {args.steps} steps, {ms_serial:.2f} ms/step (overlap off, events on)")
 
     score_ms, score_n = prof["score"]
     topk_ms, topk_n = prof["topk"]
@@ -227,6 +248,10 @@ def main():
     pool_gbs = pool_bytes * S / (pool_ms / 1000.0) / 1e9 if pool_ms > 0 else 0.0
 
     traffic = score_traffic(wl.name)
+    pitch = ((sel.max_pools + 63) // 64) * 64
+    cap_rows = (1 << 31) // (pitch * 4)
+    buf_rows = sel.workspace.numel() // ((pitch + pitch // 16) * 4)
+    chunk_rows = int(min(cap_rows, buf_rows // 2 if (args.overlap == "on" and buf_rows >= 2) else buf_rows))
     result = {
         "metric": "query-pool scores/s + selection wall time at 512k tokens, % MFMA/HBM peak",
         "value": pairs / (ms_step / 1000.0),
@@ -245,7 +270,8 @@ def main():
                          f"H={wl.H}, D={wl.D}, kpool={wl.kpool}, budget={wl.budget} pools, causal"),
             "tokens": wl.T, "rows": rows, "H": wl.H, "D": wl.D, "kpool": wl.kpool,
             "budget": wl.budget, "visible_pairs": pairs, "seed": args.seed,
-            "score_chunk_rows": int(sel.workspace.numel() // (((sel.max_pools + 63) // 64) * 64 * 4)),
+            "score_chunk_rows": chunk_rows,
+            "chunk_overlap": args.overlap,
         },
         "roofline": {
             "bound": "mfma",
@@ -261,7 +287,10 @@ def main():
             "launches_per_step": score_n // S,
             "flops_per_launch": flops / max(1, score_n // S),
             "avg_launch_ms": score_ms / max(1, score_n),
+            "measured": ("HIP events around each launch on its stream, kernel pass of the same "
+                         "steps with chunk overlap off"),
         },
+        "kernel_pass_ms_per_step": ms_serial,
         "kernels": {
             "score": {"ms_per_step": score_ms / S, "tflops": score_tflops,
                       "mfma_frac": score_tflops / PEAK_BF16_TFLOPS},

@@ -33,9 +33,12 @@
  *     in kpool_last_error() (thread-local).  Nothing is thrown across the ABI.
  *     Launch failures map to KPOOL_EHIP; faults that happen while a kernel
  *     runs surface at the caller's next synchronisation.
- *   - Calls on one stream are ordered; the library holds no global state
- *     except the optional profiler below, so concurrent calls on different
- *     streams are independent.
+ *   - Calls on one stream are ordered.  The library's only global state is
+ *     the optional profiler below and, per device, one helper stream (default
+ *     priority) with two events that kpool_score_topk uses to overlap chunks;
+ *     they are created on first use and live until the process ends.  The
+ *     helper joins back into the caller's stream before the call returns, so
+ *     results are ordered on the caller's stream as usual.
  */
 #ifndef KPOOL_H
 #define KPOOL_H
@@ -84,8 +87,20 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host,
  * chunk, one fp32 score row at a pitch of max_pools rounded up to 64 plus one
  * fp32 maximum per 16 pools of it; the score rows of a chunk are capped at
  * 2 GiB (Megatron-LM PR #8299 "Change": the chunked score path caps its score
- * buffer at 2 GiB).  Returns 0 for an empty range. */
+ * buffer at 2 GiB).  The size returned covers two such chunks when the range
+ * needs more than one, so that chunks can alternate between two buffers (see
+ * kpool_set_overlap).  Returns 0 for an empty range. */
 size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools);
+
+/* Process-wide switch for the chunk overlap of kpool_score_topk (default on).
+ * On: a workspace of two rows or more is split into two chunk buffers and
+ * consecutive chunks alternate between the caller's stream and the helper
+ * stream, so one chunk's selection runs beside the next chunk's scoring.
+ * Off: one buffer, every launch on the caller's stream, one after the other
+ * (each kernel then runs alone, which per-kernel timing needs).  Results are
+ * the same either way.  Takes effect at the next kpool_score_topk call;
+ * returns the previous setting (0 or 1). */
+int kpool_set_overlap(int on);
 
 /* Step 2 - score and select, for the global rows [q_lo, q_hi).
  * (Megatron-LM PR #8299 "Change": one rank's contiguous slice of query rows
@@ -97,9 +112,12 @@ size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools);
  *   scale    > 0, usually 1/sqrt(D)
  *   budget   pools kept per row, 1..1024 (index_topk / kpool)
  *   workspace, workspace_bytes: device scratch of at least one row
- *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools)); rows are
- *            processed in chunks of as many rows as both the 2 GiB score cap
- *            and the workspace allow.  Contents are scratch on return.
+ *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools)).  With the
+ *            overlap on (kpool_set_overlap), a workspace of two rows or more is
+ *            split into two chunk buffers and chunks alternate between the
+ *            caller's stream and the helper stream; each chunk has as many rows
+ *            as the 2 GiB score cap and its buffer allow.  Contents are scratch
+ *            on return.
  *   pool_ids int32 [q_hi - q_lo, budget] output: sequence-local pool ids,
  *            best first by (score desc, pool asc), -1 after the visible pools
  *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.

@@ -10,6 +10,9 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -86,6 +89,38 @@ int hip_fail(const char *fn, hipError_t e) {
   return fail(KPOOL_EHIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
 }
 
+// ---------------------------------------------------------------------------
+// Per-device helper stream and fork/join events for the two-buffer chunk loop.
+// Created on first use (default priority, non-blocking) and kept until the
+// process ends; g_aux_mu serialises their use across host threads.
+// ---------------------------------------------------------------------------
+struct Aux {
+  hipStream_t helper = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_aux_mu;
+std::map<int, Aux> g_aux;
+std::atomic<int> g_overlap{1};  // process-wide: two chunk buffers on two streams
+
+hipError_t get_aux(hipStream_t stream, Aux **out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  Aux &a = g_aux[dev];
+  if (!a.helper) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&a.helper, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+  }
+  *out = &a;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,8 +177,11 @@ size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools) {
   if (q_hi <= q_lo || max_pools <= 0) return 0;
   const int64_t ld = pitch_of(max_pools);
   const int64_t cap_rows = std::max<int64_t>(1, kChunkCapBytes / (ld * 4));
-  return (size_t)(std::min<int64_t>(q_hi - q_lo, cap_rows) * ws_row_bytes(ld));
+  // two full chunk buffers when the rows need more than one chunk
+  return (size_t)(std::min<int64_t>(q_hi - q_lo, 2 * cap_rows) * ws_row_bytes(ld));
 }
+
+int kpool_set_overlap(int on) { return g_overlap.exchange(on ? 1 : 0); }
 
 int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
                      const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev, int32_t nseq,
@@ -178,16 +216,24 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
     return fail(KPOOL_EWORKSPACE, "%s: workspace must hold one score row (%lld bytes), got %zu", fn,
                 (long long)row_bytes, workspace_bytes);
   if (!aligned16(workspace)) return fail(KPOOL_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-  // rows per chunk: the fp32 score buffer stays within 2 GiB and the workspace
+  // Two chunk buffers when the workspace holds at least two rows: chunks then alternate
+  // between the caller's stream and a helper stream, so one chunk's selection and the
+  // next chunk's scoring overlap instead of draining the GPU between launches.  Each
+  // buffer's fp32 score rows stay within the 2 GiB cap.
+  const int nbuf = (g_overlap.load() && (int64_t)workspace_bytes >= 2 * row_bytes) ? 2 : 1;
   const int64_t chunk_rows = std::max<int64_t>(
-      1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / row_bytes));
-  float *ws = (float *)workspace;
-  float *gws = ws + chunk_rows * ld;  // group maxima follow the score rows
+      1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / nbuf / row_bytes));
+  const int64_t nchunks = (q_hi - q_lo + chunk_rows - 1) / chunk_rows;
+  float *ws_buf[2], *gws_buf[2];
+  for (int b = 0; b < 2; ++b) {
+    ws_buf[b] = (float *)((char *)workspace + (b % nbuf) * chunk_rows * row_bytes);
+    gws_buf[b] = ws_buf[b] + chunk_rows * ld;  // group maxima follow the score rows
+  }
   hipStream_t st = (hipStream_t)stream;
   const int tile_rows = kpool::score_tile_rows();
 
-  for (int64_t c0 = q_lo; c0 < q_hi; c0 += chunk_rows) {
-    const int64_t c1 = std::min(q_hi, c0 + chunk_rows);
+  // score + select of rows [c0, c1) into one buffer, on one stream
+  auto enqueue_chunk = [&](int64_t c0, int64_t c1, float *ws, float *gws, hipStream_t cs) -> hipError_t {
     // sequences overlapping [c0, c1): one segment each, cut into row tiles
     struct Seg { int32_t lo, hi, start, pool_base; };
     std::vector<Seg> segs;
@@ -218,25 +264,53 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
       int64_t pseg = (max_npv + want_segs - 1) / want_segs;
       pseg = std::min<int64_t>(kPoolSegMax, std::max<int64_t>(64, (pseg + 63) / 64 * 64));
       const int32_t npseg = (int32_t)((max_npv + pseg - 1) / pseg);
-      hipError_t e = timed(1, st, [&] {
+      hipError_t e = timed(1, cs, [&] {
         return kpool::launch_score(H, D, q, kp, w, scale, kpool, L, ntiles, npseg, (int32_t)pseg,
-                                   c0, ld, ws, ldg, gws, st);
+                                   c0, ld, ws, ldg, gws, cs);
       });
-      if (e != hipSuccess) return hip_fail(fn, e);
+      if (e != hipSuccess) return e;
     }
-    hipError_t e = timed(2, st, [&] {
+    hipError_t e = timed(2, cs, [&] {
       return kpool::launch_topk(ws, ld, c1 - c0, nullptr, cu_seqlens_dev, nseq, c0, kpool, budget,
-                                pool_ids + (c0 - q_lo) * budget, gws, ldg, st);
+                                pool_ids + (c0 - q_lo) * budget, gws, ldg, cs);
     });
-    if (e != hipSuccess) return hip_fail(fn, e);
+    if (e != hipSuccess) return e;
     if (scores_out) {
-      e = timed(4, st, [&] {
+      e = timed(4, cs, [&] {
         return kpool::launch_scores_copy(ws, ld, c1 - c0, cu_seqlens_dev, nseq, c0, kpool,
-                                         scores_out + (c0 - q_lo) * max_pools, max_pools, st);
+                                         scores_out + (c0 - q_lo) * max_pools, max_pools, cs);
       });
+    }
+    return e;
+  };
+
+  if (nbuf == 1 || nchunks == 1) {
+    for (int64_t c0 = q_lo; c0 < q_hi; c0 += chunk_rows) {
+      hipError_t e = enqueue_chunk(c0, std::min(q_hi, c0 + chunk_rows), ws_buf[0], gws_buf[0], st);
       if (e != hipSuccess) return hip_fail(fn, e);
     }
+    return ok();
   }
+  // chunk c goes to buffer c % 2 on stream c % 2; chunk c + 2 reuses the buffer after
+  // chunk c's selection because both sit on the same stream
+  std::lock_guard<std::mutex> guard(g_aux_mu);
+  Aux *aux = nullptr;
+  hipError_t e = get_aux(st, &aux);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  hipStream_t streams[2] = {st, aux->helper};
+  e = hipEventRecord(aux->fork, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(aux->helper, aux->fork, 0);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  hipError_t first_err = hipSuccess;
+  int64_t c = 0;
+  for (int64_t c0 = q_lo; c0 < q_hi && first_err == hipSuccess; c0 += chunk_rows, ++c)
+    first_err = enqueue_chunk(c0, std::min(q_hi, c0 + chunk_rows), ws_buf[c & 1], gws_buf[c & 1],
+                              streams[c & 1]);
+  // join: the caller's stream waits for the helper whatever happened above
+  e = hipEventRecord(aux->join, aux->helper);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st, aux->join, 0);
+  if (first_err != hipSuccess) return hip_fail(fn, first_err);
+  if (e != hipSuccess) return hip_fail(fn, e);
   return ok();
 }
 

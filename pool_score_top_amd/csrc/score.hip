@@ -38,7 +38,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
+#ifndef KPOOL_SCORE_WAVES
+#define KPOOL_SCORE_WAVES 8
+#endif
+constexpr int kWaves = KPOOL_SCORE_WAVES;  // waves per workgroup
 constexpr int kRowsPerWave = 4;  // the 4-row swap reduction needs exactly 4
 constexpr int kTileRows = kWaves * kRowsPerWave;
 constexpr int kStagePools = 64;
@@ -165,6 +168,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
             16, 0, 0);
 #else
         (void)pool;
+        (void)kps;
 #endif
       }
     }

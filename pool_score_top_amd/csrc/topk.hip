@@ -7,19 +7,22 @@
 //
 // Each element is ranked by the 64-bit key (order_key(score) << 32 | ~index):
 // a larger key is better, and keys are unique, so "the best `budget` keys" is
-// exactly the selection.  One 1024-thread workgroup owns one row:
+// exactly the selection.  One 512-thread workgroup owns one row, and four of
+// them share a CU, so four rows' memory latencies overlap:
 //
-//   pass 1  (HBM)   every thread takes the max key of its elements.  In each
-//                   wave the ceil(budget/16)-th largest of the 64 maxima is
-//                   found by a register bitonic sort; the minimum L over the 16
-//                   waves is a lower bound on the budget-th best key (at least
-//                   budget distinct elements reach it).
-//   pass 2  (L2)    elements with key >= L are appended to an LDS candidate
+//   pass 1  (HBM)   every thread keeps two maxima over disjoint halves of its
+//                   elements (or, for long rows, of its 16-pool group maxima,
+//                   written by the score kernel).  In each wave the
+//                   ceil(budget/8)-th largest of its 128 maxima is found by a
+//                   register bitonic sort; the minimum L over the 8 waves is a
+//                   lower bound on the budget-th best key (at least budget
+//                   distinct elements reach it).
+//   pass 2  (L2)    elements with key >= L (for long rows: only inside the
+//                   groups whose max reaches L) are appended to an LDS candidate
 //                   list with one atomic per wave per step.  For iid scores the
-//                   list holds about 0.7 x 1024 + budget/2 entries, whatever the
-//                   row length.
+//                   list holds about a thousand entries, whatever the row length.
 //   sort            bitonic sort of the candidates (descending 64-bit keys):
-//                   distances < 64 via lane shuffles, < 1024 via LDS, larger
+//                   distances < 64 via lane shuffles, < 512 via LDS, larger
 //                   inside a thread's registers; the first `budget` are written.
 //   fallback        if the list overflows (heavy ties), an exact radix select
 //                   over the 64-bit keys (8-bit digits, re-reading the row)
@@ -32,9 +35,12 @@
 namespace kpool {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWavesT = kThreads / 64;
-constexpr int kCandCap = 4096;
+constexpr int kCandCap = 2048;   // candidate keys held in LDS
+constexpr int kGroupCap = 2048;  // candidate 16-pool groups held in LDS
+constexpr int kRound = 8;        // group maxima loaded per thread before use
+constexpr int kPieces = 4;       // 16-byte score pieces loaded per thread before use
 
 __device__ inline uint64_t compose(uint32_t okey, uint32_t idx) {
   return ((uint64_t)okey << 32) | (uint64_t)(~idx);
@@ -46,23 +52,33 @@ __device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// 64 values of a wave sorted descending; lane r returns the r-th largest.
-__device__ inline uint32_t wave_sort_desc(uint32_t v, int lane) {
+// 128 values of a wave (element e = i*64 + lane in x[i]) sorted descending in place:
+// afterwards x[i] of lane l holds the (i*64 + l)-th largest.
+__device__ inline void wave_sort128_desc(uint32_t (&x)[2], int lane) {
 #pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
+  for (int k = 2; k <= 128; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint32_t p = __shfl_xor(v, j);
-      const bool lower = (lane & j) == 0;
-      const bool desc = (lane & k) == 0;
-      v = (lower == desc) ? max(v, p) : min(v, p);
+      if (j == 64) {  // only in the last merge (k == 128): the pair is in one lane
+        const uint32_t a = x[0], b = x[1];
+        x[0] = max(a, b);
+        x[1] = min(a, b);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int e = i * 64 + lane;
+          const uint32_t p = __shfl_xor(x[i], j);
+          const bool lower = (e & j) == 0;
+          const bool desc = (e & k) == 0;
+          x[i] = (lower == desc) ? max(x[i], p) : min(x[i], p);
+        }
+      }
     }
   }
-  return v;
 }
 
-// Bitonic sort (descending) of 1024*M keys; thread tid holds elements
-// tid + 1024*m.  buf is an LDS scratch of 1024*M keys.
+// Bitonic sort (descending) of kThreads*M keys; thread tid holds elements
+// tid + kThreads*m.  buf is an LDS scratch of kThreads*M keys.
 template <int M>
 __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
   constexpr int N = kThreads * M;
@@ -124,10 +140,6 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
   }
 }
 
-constexpr int kGroupCap = 4096;  // candidate 16-pool groups held in LDS
-constexpr int kRound = 8;        // group maxima loaded per thread before use
-constexpr int kPieces = 4;       // 16-byte score pieces loaded per thread before use
-
 struct Smem {
   uint64_t cand[kCandCap];
   uint32_t glist[kGroupCap];
@@ -156,9 +168,32 @@ __device__ inline uint32_t wave_reserve(uint32_t c, uint32_t *counter, int lane)
   return __shfl(base, 0) + pre;
 }
 
+// Append the elements of one float4 piece at `base` whose key reaches `bound`.
+__device__ inline void append_piece(const float4 x, int64_t base, int64_t n, uint32_t bound,
+                                    Smem &sm, int lane) {
+  const float xs[4] = {x.x, x.y, x.z, x.w};
+  uint32_t keys[4];
+  bool sel[4];
+  uint32_t c = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    keys[e] = order_key(xs[e]);
+    sel[e] = (base + e < n) && keys[e] >= bound;
+    c += sel[e] ? 1u : 0u;
+  }
+  uint32_t pos = wave_reserve(c, &sm.count, lane);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (sel[e]) {
+      if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base + e));
+      ++pos;
+    }
+  }
+}
+
 // GMAX: the score kernel's per-row maxima of 16-pool groups are available (row pitch
-// ldg).  The bound then comes from the group maxima, and only the groups whose max
-// reaches it are read.
+// ldg).  For long rows the bound then comes from the group maxima, and only the
+// groups whose max reaches it are read.
 template <bool GMAX>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                         const int32_t *__restrict__ n_valid,
@@ -183,9 +218,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   const float *row = scores + r * ld;
   const float *grow = GMAX ? gmax + r * ldg : nullptr;
   const int64_t ng = (n + kGroup - 1) / kGroup;  // 16-pool groups of the row
-  // Group maxima are used when every thread gets at least one of them (so all 16
-  // waves contribute to the bound); shorter rows are read in full.
-  const bool use_groups = GMAX && n > budget && ng >= kThreads;
+  // Group maxima are used when each thread's two maxima both cover at least one of
+  // them (so every wave contributes 128 real maxima); shorter rows are read in full.
+  const bool use_groups = GMAX && n > budget && ng >= 2 * kThreads;
   int32_t *orow = out + r * (int64_t)budget;
   if (tid == 0) {
     sm.count = 0;
@@ -193,25 +228,25 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   }
 
   // ---- pass 1: lower bound on the budget-th best key ----------------------
-  // Thread maxima over disjoint parts of the row (its elements, or its groups' maxima,
-  // which are elements too), so any budget of them are distinct elements.
+  // Two maxima per thread over disjoint parts of the row (its elements, or its
+  // groups' maxima, which are elements too), so any budget of them are distinct
+  // elements.
   uint32_t bound = 0;
   if (n > budget) {
-    uint32_t tmax = 0;
+    uint32_t tmax[2] = {0, 0};
     if (use_groups) {
-      // rounds of kRound independent loads per thread
+      // rounds of kRound independent loads per thread; item j goes to maximum j & 1
       for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
         float v[kRound];
 #pragma unroll
-        for (int j = 0; j < kRound; ++j) {
-          const int64_t g = gb + tid + (int64_t)j * kThreads;
-          v[j] = grow[min(g, ng - 1)];
-        }
+        for (int j = 0; j < kRound; ++j)
+          v[j] = grow[min(gb + tid + (int64_t)j * kThreads, ng - 1)];
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
-          if (gb + tid + (int64_t)j * kThreads < ng) tmax = max(tmax, order_key(v[j]));
+          if (gb + tid + (int64_t)j * kThreads < ng) tmax[j & 1] = max(tmax[j & 1], order_key(v[j]));
       }
     } else {
+      // elements 0,1 of each float4 go to maximum 0, elements 2,3 to maximum 1
       for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
         const int64_t base = wbase + 4 * lane;
         if (base < n) {
@@ -219,13 +254,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
           const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (base + e < n) tmax = max(tmax, order_key(xs[e]));
+            if (base + e < n) tmax[e >> 1] = max(tmax[e >> 1], order_key(xs[e]));
         }
       }
     }
-    const uint32_t sorted = wave_sort_desc(tmax, lane);
-    const int rank = (budget + kWavesT - 1) / kWavesT;
-    const uint32_t wb = __shfl(sorted, rank - 1);
+    wave_sort128_desc(tmax, lane);
+    const int rank = (budget + kWavesT - 1) / kWavesT;  // 1..128 for budget <= 1024
+    const uint32_t pick = (rank - 1) < 64 ? tmax[0] : tmax[1];
+    const uint32_t wb = __shfl(pick, (rank - 1) & 63);
     if (lane == 0) sm.wave_bound[wave] = wb;
     __syncthreads();
     bound = sm.wave_bound[0];
@@ -240,10 +276,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
       float v[kRound];
 #pragma unroll
-      for (int j = 0; j < kRound; ++j) {
-        const int64_t g = gb + tid + (int64_t)j * kThreads;
-        v[j] = grow[min(g, ng - 1)];
-      }
+      for (int j = 0; j < kRound; ++j)
+        v[j] = grow[min(gb + tid + (int64_t)j * kThreads, ng - 1)];
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
         const int64_t g = gb + tid + (int64_t)j * kThreads;
@@ -269,64 +303,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
           x[j] = *reinterpret_cast<const float4 *>(row + (base[j] < n ? base[j] : 0));
         }
 #pragma unroll
-        for (int j = 0; j < kPieces; ++j) {
-          const float xs[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
-          uint32_t keys[4];
-          bool sel[4];
-          uint32_t c = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            keys[e] = order_key(xs[e]);
-            sel[e] = (base[j] + e < n) && keys[e] >= bound;
-            c += sel[e] ? 1u : 0u;
-          }
-          uint32_t pos = wave_reserve(c, &sm.count, lane);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (sel[e]) {
-              if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base[j] + e));
-              ++pos;
-            }
-          }
-        }
+        for (int j = 0; j < kPieces; ++j) append_piece(x[j], base[j], n, bound, sm, lane);
       }
     }
   } else {
-  for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
-    const int64_t base = wbase + 4 * lane;
-    uint32_t keys[4] = {0, 0, 0, 0};
-    bool sel[4] = {false, false, false, false};
-    uint32_t c = 0;
-    if (base < n) {
-      const float4 x = *reinterpret_cast<const float4 *>(row + base);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        keys[e] = order_key(xs[e]);
-        sel[e] = (base + e < n) && keys[e] >= bound;
-        c += sel[e] ? 1u : 0u;
-      }
+    for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
+      const int64_t base = wbase + 4 * lane;
+      const float4 x = base < n ? *reinterpret_cast<const float4 *>(row + base)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      append_piece(x, base, n, bound, sm, lane);
     }
-    const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
-    const uint32_t tot = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
-    if (tot) {
-      const uint32_t pre =
-          __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u)) +
-          2u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u)) +
-          4u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0u));
-      uint32_t wbase_pos = 0;
-      if (lane == 0) wbase_pos = atomicAdd(&sm.count, tot);
-      wbase_pos = __shfl(wbase_pos, 0);
-      uint32_t pos = wbase_pos + pre;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (sel[e]) {
-          if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base + e));
-          ++pos;
-        }
-      }
-    }
-  }
   }
   __syncthreads();
   uint32_t count = sm.count;
@@ -388,23 +374,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
           c += sel[e] ? 1u : 0u;
         }
       }
-      const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
-      const uint32_t tot = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
-      if (tot) {
-        const uint32_t pre =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u)) +
-            2u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u)) +
-            4u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0u));
-        uint32_t wbase_pos = 0;
-        if (lane == 0) wbase_pos = atomicAdd(&sm.count, tot);
-        wbase_pos = __shfl(wbase_pos, 0);
-        uint32_t pos = wbase_pos + pre;
+      uint32_t pos = wave_reserve(c, &sm.count, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (sel[e]) {
-            if (pos < (uint32_t)kCandCap) sm.cand[pos] = cks[e];
-            ++pos;
-          }
+      for (int e = 0; e < 4; ++e) {
+        if (sel[e]) {
+          if (pos < (uint32_t)kCandCap) sm.cand[pos] = cks[e];
+          ++pos;
         }
       }
     }
@@ -412,8 +387,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     count = min(sm.count, (uint32_t)kCandCap);
   }
 
-  if (count <= 1024u) sort_and_write<1>(sm.cand, count, budget, orow, tid);
-  else if (count <= 2048u) sort_and_write<2>(sm.cand, count, budget, orow, tid);
+  // the sort must also cover every output slot (missing ones are written as -1)
+  const uint32_t span = max(count, (uint32_t)budget);
+  if (span <= (uint32_t)kThreads) sort_and_write<1>(sm.cand, count, budget, orow, tid);
+  else if (span <= 2u * kThreads) sort_and_write<2>(sm.cand, count, budget, orow, tid);
   else sort_and_write<4>(sm.cand, count, budget, orow, tid);
 }
 

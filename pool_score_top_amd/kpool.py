@@ -43,6 +43,7 @@ def lib():
         "kpool_count_pools": (i64, [vp, i32, i32, vp, vp]),
         "kpool_pool_keys": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
         "kpool_workspace_bytes": (sz, [i64, i64, i32]),
+        "kpool_set_overlap": (ctypes.c_int, [ctypes.c_int]),
         "kpool_score_topk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i64, i64,
                                             i32, vp, sz, vp, vp, vp]),
         "kpool_expand": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, i64, i32, vp, vp]),
@@ -111,6 +112,12 @@ def count_pools(cu_seqlens, kpool: int):
 
 def workspace_bytes(q_lo: int, q_hi: int, max_pools: int) -> int:
     return int(lib().kpool_workspace_bytes(q_lo, q_hi, max_pools))
+
+
+def set_overlap(on: bool) -> bool:
+    """Process-wide chunk overlap of score_topk (two buffers on two streams); returns
+    the previous setting.  Off serialises every launch on the caller's stream."""
+    return bool(lib().kpool_set_overlap(1 if on else 0))
 
 
 def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None, stream=None):

@@ -35,12 +35,24 @@ def test_library_exports_every_declared_symbol():
     assert K.version() == 100
 
 
+def test_set_overlap_returns_previous_setting():
+    prev = K.set_overlap(False)
+    try:
+        assert K.set_overlap(False) is False
+        assert K.set_overlap(True) is False
+        assert K.set_overlap(True) is True
+    finally:
+        K.set_overlap(prev)
+
+
 def test_count_pools_and_workspace():
     cu_pools, mx, tot = K.count_pools([0, 9, 9, 37], 4)
     assert cu_pools.tolist() == [0, 3, 3, 10] and mx == 7 and tot == 10
     # 512k tokens, kpool 4: pitch 131072 floats = 512 KiB per row -> 4096 rows per 2 GiB chunk,
-    # plus one fp32 group maximum per 16 pools of each row
-    assert K.workspace_bytes(0, 524288, 131072) == 4096 * (131072 + 8192) * 4
+    # plus one fp32 group maximum per 16 pools of each row; two chunk buffers when the
+    # range needs more than one chunk
+    assert K.workspace_bytes(0, 524288, 131072) == 2 * 4096 * (131072 + 8192) * 4
+    assert K.workspace_bytes(0, 6000, 131072) == 6000 * (131072 + 8192) * 4
     assert K.workspace_bytes(0, 100, 131072) == 100 * (131072 + 8192) * 4
     assert K.workspace_bytes(5, 5, 10) == 0
     assert K.workspace_bytes(0, 3, 1) == 3 * (64 + 4) * 4   # pitch rounds up to 64
