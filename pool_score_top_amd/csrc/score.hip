@@ -18,9 +18,10 @@
 //     walks one segment of the pool axis, staging 64 pooled keys at a time
 //     through double-buffered LDS (one barrier per stage), so each pooled key
 //     fetched from L2 feeds 32 rows x 32 heads of MFMA work.
-//   * Causal skipping: a tile only visits pools visible to its last row, and a
-//     wave skips 16-pool sub-tiles beyond its own last row.  Scores are stored
-//     only for visible (row, pool) pairs; the selection reads nothing else.
+//   * Causal skipping: a tile only visits pools visible to its last row.  Each
+//     row's scores are stored in 16-byte pieces up to its own visible count (the
+//     last piece may run past it; the selection reads each row only up to its
+//     visible count).
 //   * The head dim is split across the 4 lane groups as contiguous runs of
 //     D/4 (a fixed permutation of K applied to q and kp alike), so every lane
 //     reads 16-byte contiguous pieces.
@@ -65,15 +66,6 @@ struct Shape {
 __device__ inline float swap16_sum(float a, float b) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Max over each 16-lane row, in every lane: quad swaps, then half-row and row mirrors (DPP).
-__device__ inline float max16(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
-  return v;
 }
 
 template <int H, int D>
@@ -142,10 +134,13 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // ---- pooled-key stages through LDS ---------------------------------------
   // Keys go global -> LDS with direct DMA loads (global_load_lds_dwordx4): one wave
   // instruction fills one contiguous 1 KiB region, lane i writing bytes [16i, 16i+16).
-  // Within a key row, 16-byte slot j holds chunk j ^ (pool mod NSLOT) of the key, an XOR
-  // swizzle that keeps the B-fragment reads of 16 consecutive pools on distinct banks.
-  // Loads are clamped and unconditional: pools past p_end are never stored, and chunks
-  // past D (padding of the K step) meet zero q fragments, so duplicates are harmless.
+  // Within a key row, 16-byte slot j holds chunk j ^ swz(pool) of the key, swz(pool) =
+  // (pool / 4) mod NSLOT: an XOR swizzle that puts the B-fragment reads of one sub-tile
+  // (pools 4c + sub of the stage, c = 0..15) on distinct banks.
+  // Loads are clamped and unconditional: pools past p_end repeat pool p_end - 1 (their
+  // scores are finite and never read), and chunks past D (padding of the K step) meet
+  // zero q fragments, so duplicates are harmless.
+  auto swz = [](int pool) { return (pool >> 2) & (S::NSLOT - 1); };
   int dma_pool[S::RPW], dma_off[S::RPW];
 #pragma unroll
   for (int i = 0; i < S::RPW; ++i) {
@@ -153,7 +148,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     const int byte = region * 1024 + lane * 16;
     dma_pool[i] = byte / S::ROWB;
     const int slot = (byte % S::ROWB) / 16;
-    dma_off[i] = min((slot ^ (dma_pool[i] % S::NSLOT)) * 8, D - 8);
+    dma_off[i] = min((slot ^ swz(dma_pool[i])) * 8, D - 8);
   }
   auto dma_stage = [&](int stage_base, int buf) {
 #pragma unroll
@@ -174,28 +169,32 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     }
   };
   // B fragment of (pool row `pl` of a stage, chunk `c`) under the swizzle
-  auto b_addr = [&](int pl, int c) { return pl * S::ROWB + ((c ^ (pl % S::NSLOT)) * 16); };
+  auto b_addr = [&](int pl, int c) { return pl * S::ROWB + ((c ^ swz(pl)) * 16); };
 
-  // One stage's scores stay in registers (one value per lane per 16-pool sub-tile) and
-  // are stored after the stage's barrier: stores are then issued before the next
-  // stage's key fetch, so waiting for that fetch never waits on fresh stores.
+  // Sub-tile `sub` of a stage holds the pools 4c + sub (c = 0..15, the MFMA column), so
+  // after the 4 sub-tiles a lane owns 4 consecutive pools of its row and stores them with
+  // one 16-byte store.  A stage's scores stay in registers and are stored after the
+  // stage's barrier: stores are then issued before the next stage's key fetch, so
+  // waiting for that fetch never waits on fresh stores.
   constexpr int kSubs = kStagePools / kSub;
+  static_assert(kSubs == 4, "one 16-byte store per lane per stage");
   // Every stage computes all its sub-tiles (no branches between the LDS prefetches and
-  // the MFMAs); only pools visible to the lane's row and inside this workgroup's pool
-  // segment are stored, so columns of neighbouring segments are never touched.
+  // the MFMAs).  A lane stores its 4 pools when the first is visible to its row; pools
+  // past the row's visible count then receive finite values that the selection never
+  // reads (it reads each row only up to its visible count), and they stay inside this
+  // workgroup's 64-aligned stage, so columns of neighbouring segments are never touched.
   // Alongside the scores, the max of every 16-pool group of a row (over its visible
   // pools) goes to `gmax`; the selection reads those first and then only the groups
   // that can hold a winner.
-  const int store_lim = min(my_nvis, p_end);
-  float vals[kSubs], gvals[kSubs];
+  const bool row_ok = wr0 + lg < nrows;
+  const int store_lim = row_ok ? min(my_nvis, p_end) : 0;
+  float vals[kSubs], gval = 0.0f;
   int st_base = -(1 << 30);  // the stage whose scores are pending in vals (none yet)
   auto flush = [&]() {
-#pragma unroll
-    for (int sub = 0; sub < kSubs; ++sub) {
-      const int p = st_base + sub * kSub + lc;
-      if (p >= 0 && p < store_lim) orow[p] = vals[sub];
-      const int g0 = st_base + sub * kSub;
-      if (lc == 0 && g0 >= 0 && g0 < store_lim) grow_max[g0 / kSub] = gvals[sub];
+    const int p0 = st_base + 4 * lc;
+    if (p0 >= 0 && p0 < store_lim) {
+      *reinterpret_cast<float4 *>(orow + p0) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+      if ((lc & 3) == 0) grow_max[p0 / kSub] = gval;
     }
   };
 
@@ -207,54 +206,59 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     flush();
     if (st + 1 < nstage) dma_stage(stage_base + kStagePools, (st + 1) & 1);
     const unsigned char *sb = lds + (st & 1) * S::STAGE_BYTES;
-    // B fragments are read one sub-tile ahead (unconditionally: reading a sub-tile this
-    // wave then skips is harmless), so LDS latency hides behind the current MFMAs.
+    // B fragments are read one sub-tile ahead, so LDS latency hides behind the MFMAs.
     bf16x8 bb[2][S::KS];
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks)
-      bb[0][ks] = *reinterpret_cast<const bf16x8 *>(sb + b_addr(lc, lg * (S::KG / 8) + ks));
+      bb[0][ks] = *reinterpret_cast<const bf16x8 *>(sb + b_addr(4 * lc, lg * (S::KG / 8) + ks));
 #pragma unroll
     for (int sub = 0; sub < kSubs; ++sub) {
       if (sub + 1 < kSubs) {
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks)
           bb[(sub + 1) & 1][ks] = *reinterpret_cast<const bf16x8 *>(
-              sb + b_addr((sub + 1) * kSub + lc, lg * (S::KG / 8) + ks));
+              sb + b_addr(4 * lc + sub + 1, lg * (S::KG / 8) + ks));
       }
-      {
-        const bf16x8 (&b)[S::KS] = bb[sub & 1];
-        // all (row, M block) accumulators advance together: 8 independent MFMAs per K step
-        floatx4 acc[kRowsPerWave][S::MB];
+      const bf16x8 (&b)[S::KS] = bb[sub & 1];
+      // all (row, M block) accumulators advance together: 8 independent MFMAs per K step
+      floatx4 acc[kRowsPerWave][S::MB];
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+        for (int mb = 0; mb < S::MB; ++mb) acc[r][mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks)
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r)
 #pragma unroll
-          for (int mb = 0; mb < S::MB; ++mb) acc[r][mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks)
-#pragma unroll
-          for (int r = 0; r < kRowsPerWave; ++r)
-#pragma unroll
-            for (int mb = 0; mb < S::MB; ++mb)
-              acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], acc[r][mb], 0, 0, 0);
-        float x[kRowsPerWave];
-#pragma unroll
-        for (int r = 0; r < kRowsPerWave; ++r) {
-          x[r] = 0.0f;
-#pragma unroll
           for (int mb = 0; mb < S::MB; ++mb)
+            acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], acc[r][mb], 0, 0, 0);
+      // epilogue: ReLU, head weights and the head sum
+      float x[kRowsPerWave];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(acc[r][mb][i], 0.0f), sw[r][mb][i], x[r]);
-        }
-        // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
-        const float y01 = swap16_sum(x[0], x[1]);
-        const float y23 = swap16_sum(x[2], x[3]);
-        // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
-        auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
-        const float v = __uint_as_float(z[0]) + __uint_as_float(z[1]);
-        vals[sub] = v;
-        gvals[sub] = max16(stage_base + sub * kSub + lc < my_nvis ? v : -__builtin_inff());
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        x[r] = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(acc[r][mb][i], 0.0f), sw[r][mb][i], x[r]);
       }
+      // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
+      const float y01 = swap16_sum(x[0], x[1]);
+      const float y23 = swap16_sum(x[2], x[3]);
+      // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
+      auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
+      vals[sub] = __uint_as_float(z[0]) + __uint_as_float(z[1]);
     }
+    // max of each 16-pool group over the row's visible pools: 4 own values, then the
+    // 4 lanes of the quad (pools 16j .. 16j + 15 of the stage sit in lanes 4j .. 4j + 3)
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int sub = 0; sub < kSubs; ++sub)
+      m = fmaxf(m, stage_base + 4 * lc + sub < my_nvis ? vals[sub] : -__builtin_inff());
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+    gval = m;
     st_base = stage_base;
     __syncthreads();  // also waits for this wave's DMA of the next stage
   }
