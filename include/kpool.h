@@ -110,7 +110,8 @@ int kpool_set_overlap(int on);
  *   kp       bf16 [P_tot, D]   pooled keys from kpool_pool_keys
  *   w        fp32 [T, H]       per-row head weights (any sign)
  *   scale    > 0, usually 1/sqrt(D)
- *   budget   pools kept per row, 1..1024 (index_topk / kpool)
+ *   budget   pools kept per row, 1..2048 (index_topk / kpool; 2048 for the per-token
+ *            indexer, kpool = 1)
  *   workspace, workspace_bytes: device scratch of at least one row
  *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools)).  With the
  *            overlap on (kpool_set_overlap), a workspace of two rows or more is
@@ -147,6 +148,7 @@ int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host,
  *   scores   fp32 [rows, ld], ld % 4 == 0, 16-byte aligned
  *   n_valid  int32 [rows] device: row r ranks scores[r, 0 .. n_valid[r]),
  *            0 <= n_valid[r] <= ld
+ *   budget   1..2048, as for kpool_score_topk
  *   pool_ids int32 [rows, budget]: same ordering and padding as kpool_score_topk */
 int kpool_topk(const float *scores, int64_t ld, const int32_t *n_valid, int64_t rows,
                int32_t budget, int32_t *pool_ids, void *stream);

@@ -43,7 +43,7 @@ hipError_t launch_score(int H, int D, const uint16_t *q, const uint16_t *kp, con
                         int32_t npseg, int32_t pseg_pools, int64_t chunk_row0, int64_t ld,
                         float *out, int64_t ldg, float *gmax, hipStream_t stream);
 
-constexpr int kTopkMaxBudget = 1024;
+constexpr int kTopkMaxBudget = 2048;
 // Rows [row0, row0 + nrows) of `scores` (row r at scores + r*ld).  The number
 // of ranked entries of row r is n_valid[r] if n_valid is not null, else
 // (t / kpool + 1) for the row's sequence-local position t (global row

@@ -7,20 +7,22 @@
 //
 // Each element is ranked by the 64-bit key (order_key(score) << 32 | ~index):
 // a larger key is better, and keys are unique, so "the best `budget` keys" is
-// exactly the selection.  One 512-thread workgroup owns one row, and four of
-// them share a CU, so four rows' memory latencies overlap:
+// exactly the selection.  One 512-thread workgroup owns one row, and several
+// of them share a CU, so their memory latencies overlap:
 //
-//   pass 1  (HBM)   every thread keeps two maxima over disjoint halves of its
+//   pass 1  (HBM)   every thread keeps NMAX maxima over disjoint parts of its
 //                   elements (or, for long rows, of its 16-pool group maxima,
-//                   written by the score kernel).  In each wave the
-//                   ceil(budget/8)-th largest of its 128 maxima is found by a
-//                   register bitonic sort; the minimum L over the 8 waves is a
-//                   lower bound on the budget-th best key (at least budget
-//                   distinct elements reach it).
+//                   written by the score kernel): NMAX = 2 for budgets up to
+//                   1024, 8 up to 2048.  In each wave the ceil(budget/8)-th
+//                   largest of its 64*NMAX maxima is found by a register bitonic
+//                   sort; the minimum L over the 8 waves is a lower bound on the
+//                   budget-th best key (at least budget distinct elements reach
+//                   it).
 //   pass 2  (L2)    elements with key >= L (for long rows: only inside the
 //                   groups whose max reaches L) are appended to an LDS candidate
 //                   list with one atomic per wave per step.  For iid scores the
-//                   list holds about a thousand entries, whatever the row length.
+//                   list holds about 0.7 x (number of maxima) entries, whatever
+//                   the row length.
 //   sort            bitonic sort of the candidates (descending 64-bit keys):
 //                   distances < 64 via lane shuffles, < 512 via LDS, larger
 //                   inside a thread's registers; the first `budget` are written.
@@ -37,8 +39,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWavesT = kThreads / 64;
-constexpr int kCandCap = 2048;   // candidate keys held in LDS
-constexpr int kGroupCap = 2048;  // candidate 16-pool groups held in LDS
 constexpr int kRound = 8;        // group maxima loaded per thread before use
 constexpr int kPieces = 4;       // 16-byte score pieces loaded per thread before use
 
@@ -52,20 +52,28 @@ __device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// 128 values of a wave (element e = i*64 + lane in x[i]) sorted descending in place:
-// afterwards x[i] of lane l holds the (i*64 + l)-th largest.
-__device__ inline void wave_sort128_desc(uint32_t (&x)[2], int lane) {
+// 64*NMAX values of a wave (element e = i*64 + lane in x[i]) sorted descending in
+// place: afterwards x[i] of lane l holds the (i*64 + l)-th largest.
+template <int NMAX>
+__device__ inline void wave_sort_desc(uint32_t (&x)[NMAX], int lane) {
 #pragma unroll
-  for (int k = 2; k <= 128; k <<= 1) {
+  for (int k = 2; k <= 64 * NMAX; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j == 64) {  // only in the last merge (k == 128): the pair is in one lane
-        const uint32_t a = x[0], b = x[1];
-        x[0] = max(a, b);
-        x[1] = min(a, b);
+      if (j >= 64) {  // the pair sits in one lane, registers i and i ^ (j / 64)
+        const int jr = j / 64;
+#pragma unroll
+        for (int i = 0; i < NMAX; ++i) {
+          if ((i & jr) == 0) {
+            const bool desc = ((i * 64) & k) == 0;  // k >= 128: lane bits play no part
+            const uint32_t a = x[i], b = x[i | jr];
+            x[i] = desc ? max(a, b) : min(a, b);
+            x[i | jr] = desc ? min(a, b) : max(a, b);
+          }
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NMAX; ++i) {
           const int e = i * 64 + lane;
           const uint32_t p = __shfl_xor(x[i], j);
           const bool lower = (e & j) == 0;
@@ -140,9 +148,18 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
   }
 }
 
+// LDS lists sized for NMAX maxima per thread: about 0.7 x 512 x NMAX candidates are
+// expected, so the caps leave room for the spread.
+template <int NMAX>
+struct Caps {
+  static constexpr int kCand = NMAX <= 2 ? 2048 : 4096;  // candidate keys
+  static constexpr int kGroups = kCand;                   // candidate 16-pool groups
+};
+
+template <int NMAX>
 struct Smem {
-  uint64_t cand[kCandCap];
-  uint32_t glist[kGroupCap];
+  uint64_t cand[Caps<NMAX>::kCand];
+  uint32_t glist[Caps<NMAX>::kGroups];
   uint32_t hist[256];
   uint32_t wave_bound[kWavesT];
   uint64_t prefix;
@@ -169,8 +186,10 @@ __device__ inline uint32_t wave_reserve(uint32_t c, uint32_t *counter, int lane)
 }
 
 // Append the elements of one float4 piece at `base` whose key reaches `bound`.
+template <int NMAX>
 __device__ inline void append_piece(const float4 x, int64_t base, int64_t n, uint32_t bound,
-                                    Smem &sm, int lane) {
+                                    Smem<NMAX> &sm, int lane) {
+  constexpr int kCandCap = Caps<NMAX>::kCand;
   const float xs[4] = {x.x, x.y, x.z, x.w};
   uint32_t keys[4];
   bool sel[4];
@@ -194,7 +213,7 @@ __device__ inline void append_piece(const float4 x, int64_t base, int64_t n, uin
 // GMAX: the score kernel's per-row maxima of 16-pool groups are available (row pitch
 // ldg).  For long rows the bound then comes from the group maxima, and only the
 // groups whose max reaches it are read.
-template <bool GMAX>
+template <bool GMAX, int NMAX>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                         const int32_t *__restrict__ n_valid,
                                                         const int32_t *__restrict__ cu_seqlens,
@@ -202,7 +221,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
                                                         int budget, int32_t *__restrict__ out,
                                                         const float *__restrict__ gmax,
                                                         int64_t ldg) {
-  __shared__ Smem sm;
+  constexpr int kCandCap = Caps<NMAX>::kCand;
+  constexpr int kGroupCap = Caps<NMAX>::kGroups;
+  static_assert(NMAX == 2 || (NMAX % 4 == 0 && kRound % NMAX == 0), "maxima per thread");
+  __shared__ Smem<NMAX> sm;
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,9 +240,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   const float *row = scores + r * ld;
   const float *grow = GMAX ? gmax + r * ldg : nullptr;
   const int64_t ng = (n + kGroup - 1) / kGroup;  // 16-pool groups of the row
-  // Group maxima are used when each thread's two maxima both cover at least one of
-  // them (so every wave contributes 128 real maxima); shorter rows are read in full.
-  const bool use_groups = GMAX && n > budget && ng >= 2 * kThreads;
+  // Group maxima are used when each of a thread's NMAX maxima covers at least one of
+  // them (so every wave contributes 64*NMAX real maxima); shorter rows are read in full.
+  const bool use_groups = GMAX && n > budget && ng >= (int64_t)NMAX * kThreads;
   int32_t *orow = out + r * (int64_t)budget;
   if (tid == 0) {
     sm.count = 0;
@@ -228,14 +250,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   }
 
   // ---- pass 1: lower bound on the budget-th best key ----------------------
-  // Two maxima per thread over disjoint parts of the row (its elements, or its
+  // NMAX maxima per thread over disjoint parts of the row (its elements, or its
   // groups' maxima, which are elements too), so any budget of them are distinct
   // elements.
   uint32_t bound = 0;
   if (n > budget) {
-    uint32_t tmax[2] = {0, 0};
+    uint32_t tmax[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) tmax[i] = 0;
     if (use_groups) {
-      // rounds of kRound independent loads per thread; item j goes to maximum j & 1
+      // rounds of kRound independent loads per thread; item j goes to maximum j % NMAX
       for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
         float v[kRound];
 #pragma unroll
@@ -243,24 +267,36 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
           v[j] = grow[min(gb + tid + (int64_t)j * kThreads, ng - 1)];
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
-          if (gb + tid + (int64_t)j * kThreads < ng) tmax[j & 1] = max(tmax[j & 1], order_key(v[j]));
+          if (gb + tid + (int64_t)j * kThreads < ng)
+            tmax[j % NMAX] = max(tmax[j % NMAX], order_key(v[j]));
       }
     } else {
-      // elements 0,1 of each float4 go to maximum 0, elements 2,3 to maximum 1
-      for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
-        const int64_t base = wbase + 4 * lane;
-        if (base < n) {
-          const float4 x = *reinterpret_cast<const float4 *>(row + base);
-          const float xs[4] = {x.x, x.y, x.z, x.w};
+      // float4 pieces, NP per thread per step; element e of piece q goes to maximum
+      // (4q + e) * NMAX / (4 NP): 2 maxima share a piece, or 4 pieces feed 8 maxima
+      constexpr int NP = NMAX <= 4 ? 1 : NMAX / 4;
+      for (int64_t wbase = (int64_t)wave * 256 * NP; wbase < n; wbase += (int64_t)kThreads * 4 * NP) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (base + e < n) tmax[e >> 1] = max(tmax[e >> 1], order_key(xs[e]));
+        for (int q = 0; q < NP; ++q) {
+          const int64_t base = wbase + 256 * q + 4 * lane;
+          if (base < n) {
+            const float4 x = *reinterpret_cast<const float4 *>(row + base);
+            const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              constexpr int kDiv = 4 * NP / NMAX;
+              const int m = (4 * q + e) / (kDiv > 0 ? kDiv : 1);
+              if (base + e < n) tmax[m] = max(tmax[m], order_key(xs[e]));
+            }
+          }
         }
       }
     }
-    wave_sort128_desc(tmax, lane);
-    const int rank = (budget + kWavesT - 1) / kWavesT;  // 1..128 for budget <= 1024
-    const uint32_t pick = (rank - 1) < 64 ? tmax[0] : tmax[1];
+    wave_sort_desc<NMAX>(tmax, lane);
+    const int rank = (budget + kWavesT - 1) / kWavesT;  // 1..64*NMAX
+    uint32_t pick = tmax[0];
+#pragma unroll
+    for (int i = 1; i < NMAX; ++i)
+      if ((rank - 1) / 64 == i) pick = tmax[i];
     const uint32_t wb = __shfl(pick, (rank - 1) & 63);
     if (lane == 0) sm.wave_bound[wave] = wb;
     __syncthreads();
@@ -391,7 +427,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   const uint32_t span = max(count, (uint32_t)budget);
   if (span <= (uint32_t)kThreads) sort_and_write<1>(sm.cand, count, budget, orow, tid);
   else if (span <= 2u * kThreads) sort_and_write<2>(sm.cand, count, budget, orow, tid);
-  else sort_and_write<4>(sm.cand, count, budget, orow, tid);
+  else if (kCandCap <= 4 * kThreads || span <= 4u * kThreads)
+    sort_and_write<4>(sm.cand, count, budget, orow, tid);
+  else sort_and_write<(kCandCap > 4 * kThreads ? 8 : 4)>(sm.cand, count, budget, orow, tid);
 }
 
 // scores_out rows: the chunk buffer's visible scores, -inf elsewhere
@@ -415,12 +453,21 @@ hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int
                        int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
                        hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
-  if (gmax)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)nrows), dim3(kThreads), 0, stream, scores,
-                       ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+  if (budget > kTopkMaxBudget) return hipErrorInvalidValue;
+  // budgets above 1024 need more maxima per thread for a tight bound (and longer lists)
+  const bool big = budget > 1024;
+  if (gmax && big)
+    hipLaunchKernelGGL((topk_kernel<true, 8>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
+                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+  else if (gmax)
+    hipLaunchKernelGGL((topk_kernel<true, 2>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
+                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+  else if (big)
+    hipLaunchKernelGGL((topk_kernel<false, 8>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
+                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)nrows), dim3(kThreads), 0, stream, scores,
-                       ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+    hipLaunchKernelGGL((topk_kernel<false, 2>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
+                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
   return hipGetLastError();
 }
 

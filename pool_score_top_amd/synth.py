@@ -19,6 +19,8 @@ tokens; head dim 128):
   thd65536   two batches of 32768 tokens, each cut into 1..8 ragged sequences
   sq262144   one sequence of 262144 tokens
   sq524288   one sequence of 524288 tokens (and its last 1/8 row slice)
+  *_k1       the same shapes with kpool 1 (the per-token indexer: every token is a
+             pool) and budget 2048 = index_topk
 
 q and k are N(0,1) draws rounded to bf16; w is fp32.
 """
@@ -67,6 +69,11 @@ WORKLOADS = {
     "sq524288": Workload("sq524288", 524288, 32, 128, 4, 512, 32.0),
     "sq524288_slice": Workload("sq524288_slice", 524288, 32, 128, 4, 512, 32.0,
                                q_lo=7 * 524288 // 8, q_hi=524288),
+    # kpool 1: index_topk 2048 tokens = 2048 pools per row
+    "sq4096_k1": Workload("sq4096_k1", 4096, 32, 128, 1, 2048, 32.0),
+    "thd65536_k1": Workload("thd65536_k1", 65536, 32, 128, 1, 2048, 32.0, layout="thd"),
+    "sq262144_k1": Workload("sq262144_k1", 262144, 32, 128, 1, 2048, 32.0),
+    "sq524288_k1": Workload("sq524288_k1", 524288, 32, 128, 1, 2048, 32.0),
 }
 
 

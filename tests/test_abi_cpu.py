@@ -77,7 +77,7 @@ def _call_score(**kw):
     (dict(q_hi=65), K.KPOOL_EINVAL),
     (dict(q_lo=-1), K.KPOOL_EINVAL),
     (dict(budget=0), K.KPOOL_EINVAL),
-    (dict(budget=1025), K.KPOOL_EINVAL),
+    (dict(budget=2049), K.KPOOL_EINVAL),
     (dict(kpool=0), K.KPOOL_EINVAL),
     (dict(scale=0.0), K.KPOOL_EINVAL),
     (dict(scale=float("nan")), K.KPOOL_EINVAL),

@@ -88,5 +88,9 @@ def test_sq262144_sampled_rows():
     _check_sampled("sq262144", seed=0, n_random=8)
 
 
+def test_sq262144_per_token_sampled_rows():
+    _check_sampled("sq262144_k1", seed=0, n_random=6)
+
+
 def test_sq524288_sampled_rows_and_last_eighth_slice():
     _check_sampled("sq524288", seed=0, n_random=8, check_slice=True)

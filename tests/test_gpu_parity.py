@@ -110,14 +110,16 @@ def test_tiny_shapes_variants(variant):
         _full_check(synth.workload("tiny", T=300, budget=budget), r, res, where=f"{variant} b{budget}")
 
 
-def test_sq4096_workload():
-    wl, r = _inputs("sq4096", 0)
+@pytest.mark.parametrize("name", ["sq4096", "sq4096_k1"])
+def test_sq4096_workload(name):
+    wl, r = _inputs(name, 0)
     res = run_gpu(r, wl.kpool, wl.budget)
-    _full_check(wl, r, res, where="sq4096")
+    _full_check(wl, r, res, where=name)
 
 
-def test_thd_workload_windows():
-    wl, r = _inputs("thd65536", 0)
+@pytest.mark.parametrize("name", ["thd65536", "thd65536_k1"])
+def test_thd_workload_windows(name):
+    wl, r = _inputs(name, 0)
     cu = r["cu_seqlens"]
     res = run_gpu(r, wl.kpool, wl.budget, want_scores=False)
     # windows at every sequence start and end plus a spread of interior rows
@@ -143,39 +145,59 @@ def test_thd_workload_windows():
     kp_o, o_scores, t = oracle_rows(r, wl.kpool, rows, width=sel.max_pools)
     np.testing.assert_array_equal(res["kp"], kp_o)
     nvis = t // wl.kpool + 1
-    check_scores(g_scores, o_scores, nvis, "thd")
-    check_topk_self(g_scores, g_ids, nvis, wl.budget, "thd")
-    check_selection_vs_oracle(g_ids, o_scores, nvis, wl.budget, "thd")
-    check_tokens(res["token_ids"][rows], res["pool_ids"][rows], t, wl.kpool, where="thd")
+    check_scores(g_scores, o_scores, nvis, name)
+    check_topk_self(g_scores, g_ids, nvis, wl.budget, name)
+    check_selection_vs_oracle(g_ids, o_scores, nvis, wl.budget, name)
+    check_tokens(res["token_ids"][rows], res["pool_ids"][rows], t, wl.kpool, where=name)
 
 
 # ---------------------------------------------------------------------------
 # Invariants of the whole path
 # ---------------------------------------------------------------------------
 
-def test_row_split_and_chunking_reassemble_bitwise():
+@pytest.mark.parametrize("kpool,budget", [(4, 64), (1, 1100)])
+def test_row_split_and_chunking_reassemble_bitwise(kpool, budget):
     """Slices [q_lo, q_hi) with a workspace of a few rows (many chunks, slice edges inside
     chunks and tiles) concatenate to the single full run, scores and ids alike
     (Megatron-LM PR #8299, 'Test plan': sharded == unsharded, small chunk cap)."""
-    wl, r = _inputs("sq4096", 5, T=1500)
+    wl, r = _inputs("sq4096", 5, T=1500, kpool=kpool)
     r["cu_seqlens"] = np.array([0, 700, 701, 1500], dtype=np.int32)
-    full = run_gpu(r, wl.kpool, 64)
+    full = run_gpu(r, wl.kpool, budget)
     pitch = ((full["max_pools"] + 63) // 64) * 64
     row_bytes = (pitch + pitch // 16) * 4     # one score row plus its 16-pool group maxima
     for bounds, cap in [((0, 333, 334, 1000, 1500), 7 * row_bytes), ((0, 1, 700, 1499, 1500), row_bytes),
                         ((0, 750, 1500), 100 * row_bytes)]:
-        parts = [run_gpu(r, wl.kpool, 64, q_lo=a, q_hi=b, workspace_cap=cap)
+        parts = [run_gpu(r, wl.kpool, budget, q_lo=a, q_hi=b, workspace_cap=cap)
                  for a, b in zip(bounds[:-1], bounds[1:])]
         for key in ("pool_ids", "token_ids", "scores"):
             np.testing.assert_array_equal(np.concatenate([p[key] for p in parts]), full[key], err_msg=key)
     # the same chunks serialised on one stream (overlap off) give the same bits
     prev = K.set_overlap(False)
     try:
-        serial = run_gpu(r, wl.kpool, 64, workspace_cap=7 * row_bytes)
+        serial = run_gpu(r, wl.kpool, budget, workspace_cap=7 * row_bytes)
     finally:
         K.set_overlap(prev)
     for key in ("pool_ids", "token_ids", "scores"):
         np.testing.assert_array_equal(serial[key], full[key], err_msg=key)
+
+
+def test_per_token_long_rows_use_group_pruning():
+    """kpool 1, budget 2048, rows that see more than 65536 pools: the top-k reads the
+    score kernel's group maxima first (8 per thread) and then only candidate groups;
+    checked against the oracle on a window of such rows, with a small workspace so the
+    window spans several chunks."""
+    wl, r = _inputs("sq4096_k1", 11, T=67000)
+    lo, hi = 66000, 66090
+    pitch = (67000 + 63) // 64 * 64
+    res = run_gpu(r, 1, 2048, q_lo=lo, q_hi=hi, workspace_cap=20 * (pitch + pitch // 16) * 4)
+    rows = np.arange(lo, hi)
+    kp, o_scores, t = oracle_rows(r, 1, rows, width=res["max_pools"])
+    np.testing.assert_array_equal(res["kp"], kp)
+    nvis = t + 1
+    check_scores(res["scores"], o_scores, nvis, "k1 long")
+    check_topk_self(res["scores"], res["pool_ids"], nvis, 2048, "k1 long")
+    check_selection_vs_oracle(res["pool_ids"], o_scores, nvis, 2048, "k1 long")
+    check_tokens(res["token_ids"], res["pool_ids"], t, 1, where="k1 long")
 
 
 def test_thd_packing_invariance():
@@ -248,7 +270,7 @@ def _topk_rows(rng):
     return rows
 
 
-@pytest.mark.parametrize("budget", [1, 7, 512, 1024])
+@pytest.mark.parametrize("budget", [1, 7, 512, 1024, 1025, 2048])
 def test_topk_standalone_matches_oracle_selection(budget):
     rng = np.random.default_rng(budget)
     rows = _topk_rows(rng)
