@@ -23,9 +23,10 @@
 //                   list with one atomic per wave per step.  For iid scores the
 //                   list holds about 0.7 x (number of maxima) entries, whatever
 //                   the row length.
-//   sort            bitonic sort of the candidates (descending 64-bit keys):
-//                   distances < 64 via lane shuffles, < 512 via LDS, larger
-//                   inside a thread's registers; the first `budget` are written.
+//   sort            bitonic sort of the candidates (descending 64-bit keys) with
+//                   each thread holding consecutive keys: short distances inside
+//                   a thread, then lane shuffles, then LDS; the first `budget`
+//                   are written.
 //   fallback        if the list overflows (heavy ties), an exact radix select
 //                   over the 64-bit keys (8-bit digits, re-reading the row)
 //                   finds the budget-th key and collects exactly budget
@@ -85,47 +86,59 @@ __device__ inline void wave_sort_desc(uint32_t (&x)[NMAX], int lane) {
   }
 }
 
-// Bitonic sort (descending) of kThreads*M keys; thread tid holds elements
-// tid + kThreads*m.  buf is an LDS scratch of kThreads*M keys.
+// Bitonic sort (descending) of kThreads*M keys in a blocked layout: thread t holds
+// elements t*M .. t*M + M-1 in v[0..M-1].  Compare-exchange distances j < M stay in a
+// thread's registers, M <= j < 64M are lane shuffles within a wave, and only larger
+// ones go through LDS (buf: kThreads*M keys, laid out m-major so that every LDS access
+// of a wave is to consecutive keys).  Small distances are the most frequent stages of a
+// bitonic sort, so most of them cost no communication.
 template <int M>
 __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
   constexpr int N = kThreads * M;
+  const int e0 = tid * M;
 #pragma unroll 1
   for (int k = 2; k <= N; k <<= 1) {
+    // distances through LDS
 #pragma unroll 1
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= kThreads) {
-        const int jm = j / kThreads;
+    for (int j = k >> 1; j >= 64 * M; j >>= 1) {
+      const int d = j / M;
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < M; ++m) buf[m * kThreads + tid] = v[m];
+      __syncthreads();
+      const bool lower = (tid & d) == 0;
+      const bool desc = (e0 & k) == 0;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint64_t p = buf[m * kThreads + (tid ^ d)];
+        v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
+      }
+    }
+    // distances across lanes of one wave
+#pragma unroll 1
+    for (int j = min(k >> 1, 32 * M); j >= M; j >>= 1) {
+      const int d = j / M;
+      const bool lower = (tid & d) == 0;
+      const bool desc = (e0 & k) == 0;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint64_t p = shfl_xor_u64(v[m], d);
+        v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
+      }
+    }
+    // distances inside a thread
+#pragma unroll
+    for (int j = M / 2; j > 0; j >>= 1) {
+      if (j < k) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          if ((m & jm) == 0) {
-            const int m2 = m | jm;
-            const bool desc = ((tid + kThreads * m) & k) == 0;
-            const uint64_t a = v[m], b = v[m2];
-            if (desc ? (a < b) : (a > b)) { v[m] = b; v[m2] = a; }
+          if ((m & j) == 0) {
+            const bool desc = ((e0 + m) & k) == 0;
+            const uint64_t a = v[m], b = v[m | j];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[m] = sw ? b : a;
+            v[m | j] = sw ? a : b;
           }
-        }
-      } else if (j >= 64) {
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < M; ++m) buf[tid + kThreads * m] = v[m];
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const int i = tid + kThreads * m;
-          const uint64_t p = buf[i ^ j];
-          const bool lower = (i & j) == 0;
-          const bool desc = (i & k) == 0;
-          v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const int i = tid + kThreads * m;
-          const uint64_t p = shfl_xor_u64(v[m], j);
-          const bool lower = (i & j) == 0;
-          const bool desc = (i & k) == 0;
-          v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
         }
       }
     }
@@ -135,15 +148,16 @@ __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
 template <int M>
 __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32_t *orow, int tid) {
   uint64_t v[M];
+  // the starting order is free: read the list m-major (consecutive keys per wave access)
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const uint32_t i = tid + kThreads * m;
+    const uint32_t i = m * kThreads + tid;
     v[m] = i < count ? cand[i] : 0ull;  // 0 is below every real key
   }
   block_sort_desc<M>(v, cand, tid);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int i = tid + kThreads * m;
+    const int i = tid * M + m;
     if (i < budget) orow[i] = (v[m] != 0ull) ? (int32_t)(~(uint32_t)v[m]) : -1;
   }
 }
