@@ -23,6 +23,9 @@
 //                   list with one atomic per wave per step.  For iid scores the
 //                   list holds about 0.7 x (number of maxima) entries, whatever
 //                   the row length.
+//   cut             when the list is longer than budget and that would double
+//                   the sort, a radix select over the LDS list keeps exactly the
+//                   best `budget` keys.
 //   sort            bitonic sort of the candidates (descending 64-bit keys) with
 //                   each thread holding consecutive keys: short distances inside
 //                   a thread, then lane shuffles, then LDS; the first `budget`
@@ -179,6 +182,7 @@ struct Smem {
   uint64_t prefix;
   uint32_t count;
   uint32_t gcount;
+  uint32_t scount;
   int32_t pbits;
   int32_t krem;
   int32_t done;
@@ -197,6 +201,43 @@ __device__ inline uint32_t wave_reserve(uint32_t c, uint32_t *counter, int lane)
   uint32_t base = 0;
   if (lane == 0) base = atomicAdd(counter, tot);
   return __shfl(base, 0) + pre;
+}
+
+// One radix-select step, run by one whole wave: hist holds the 256 counts of the next
+// 8-bit digit among the keys that match the current prefix.  From the top digit down,
+// find the digit at which the running count reaches krem, and leave the narrowed state
+// (prefix, pbits, krem, done) in sm.  Lane L looks after digits 255-4L .. 252-4L.
+template <class SM>
+__device__ inline void next_digit(SM &sm, uint64_t prefix, int pbits, int krem, int lane) {
+  uint32_t c[4];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = sm.hist[255 - 4 * lane - i];
+    tot += c[i];
+  }
+  uint32_t incl = tot;  // inclusive prefix over lanes, i.e. over digits from the top
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const uint32_t excl = incl - tot;
+  // the digits hold at least krem keys in all, so some lane reaches it
+  const uint64_t hit = __ballot(incl >= (uint32_t)krem);
+  if (lane == __ffsll((unsigned long long)hit) - 1) {
+    uint32_t cum = excl;
+    int i = 0;
+    for (; i < 3; ++i) {
+      if (cum + c[i] >= (uint32_t)krem) break;
+      cum += c[i];
+    }
+    const int rem = krem - (int)cum;
+    sm.krem = rem;
+    sm.prefix = (prefix << 8) | (uint64_t)(255 - 4 * lane - i);
+    sm.pbits = pbits + 8;
+    sm.done = (c[i] == (uint32_t)rem) ? 1 : 0;
+  }
 }
 
 // Append the elements of one float4 piece at `base` whose key reaches `bound`.
@@ -261,6 +302,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
   if (tid == 0) {
     sm.count = 0;
     sm.gcount = 0;
+    sm.scount = 0;
   }
 
   // ---- pass 1: lower bound on the budget-th best key ----------------------
@@ -389,19 +431,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
         }
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (cum + sm.hist[d] >= (uint32_t)krem) break;
-          cum += sm.hist[d];
-        }
-        sm.krem = krem - (int)cum;
-        sm.prefix = (prefix << 8) | (uint64_t)d;
-        sm.pbits = pbits + 8;
-        sm.done = (sm.hist[d] == (uint32_t)sm.krem) ? 1 : 0;
-        sm.count = 0;
-      }
+      if (wave == 0) next_digit(sm, prefix, pbits, krem, lane);
+      if (tid == 0) sm.count = 0;
       __syncthreads();
       prefix = sm.prefix;
       pbits = sm.pbits;
@@ -437,13 +468,53 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
     count = min(sm.count, (uint32_t)kCandCap);
   }
 
+  // ---- exact cut to `budget` keys when that shrinks the sort ----------------
+  // A radix select over the LDS list (8-bit digits of the unique 64-bit keys, usually
+  // settled within a few digits) finds the budget-th key; the keys at or above it are
+  // gathered into the spare group-list space and only those are sorted.
+  auto sort_class = [](uint32_t x) { return x <= kThreads ? 1 : x <= 2 * kThreads ? 2 : x <= 4 * kThreads ? 4 : 8; };
+  uint64_t *list = sm.cand;
+  if (count > (uint32_t)budget && sort_class(count) > sort_class((uint32_t)budget)) {
+    uint64_t prefix = 0;
+    int pbits = 0;
+    int krem = budget;
+    for (int pass = 0; pass < 8; ++pass) {
+      if (tid < 256) sm.hist[tid] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < count; i += kThreads) {
+        const uint64_t ck = sm.cand[i];
+        if (pbits == 0 || (ck >> (64 - pbits)) == prefix)
+          atomicAdd(&sm.hist[(uint32_t)(ck >> (56 - pbits)) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) next_digit(sm, prefix, pbits, krem, lane);
+      __syncthreads();
+      prefix = sm.prefix;
+      pbits = sm.pbits;
+      krem = sm.krem;
+      if (sm.done) break;
+    }
+    // exactly `budget` keys have their top pbits >= prefix (pbits >= 8 here)
+    uint64_t *sel = reinterpret_cast<uint64_t *>(sm.glist);  // holds kGroupCap/2 >= budget keys
+    for (uint32_t i0 = 0; i0 < count; i0 += kThreads) {
+      const uint32_t i = i0 + tid;
+      const uint64_t ck = i < count ? sm.cand[i] : 0ull;
+      const bool take = i < count && (ck >> (64 - pbits)) >= prefix;
+      const uint32_t pos = wave_reserve(take ? 1u : 0u, &sm.scount, lane);
+      if (take) sel[pos] = ck;
+    }
+    __syncthreads();
+    list = sel;
+    count = (uint32_t)budget;
+  }
+
   // the sort must also cover every output slot (missing ones are written as -1)
   const uint32_t span = max(count, (uint32_t)budget);
-  if (span <= (uint32_t)kThreads) sort_and_write<1>(sm.cand, count, budget, orow, tid);
-  else if (span <= 2u * kThreads) sort_and_write<2>(sm.cand, count, budget, orow, tid);
+  if (span <= (uint32_t)kThreads) sort_and_write<1>(list, count, budget, orow, tid);
+  else if (span <= 2u * kThreads) sort_and_write<2>(list, count, budget, orow, tid);
   else if (kCandCap <= 4 * kThreads || span <= 4u * kThreads)
-    sort_and_write<4>(sm.cand, count, budget, orow, tid);
-  else sort_and_write<(kCandCap > 4 * kThreads ? 8 : 4)>(sm.cand, count, budget, orow, tid);
+    sort_and_write<4>(list, count, budget, orow, tid);
+  else sort_and_write<(kCandCap > 4 * kThreads ? 8 : 4)>(list, count, budget, orow, tid);
 }
 
 // scores_out rows: the chunk buffer's visible scores, -inf elsewhere
