@@ -128,11 +128,32 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   }
   // visible pools of the row this lane stores (row wr0 + lg)
   const int my_nvis = (wr0 + lg < nrows) ? (int)((t0 + wr0 + lg) / kpool) + 1 : 0;
-  float *orow = out + (row0 + min(wr0 + lg, nrows - 1) - chunk_row0) * ld;
-  float *grow_max = gmax + (row0 + min(wr0 + lg, nrows - 1) - chunk_row0) * ldg;
+  // Global accesses of the loop go through buffer resources built from wave-uniform
+  // values (forced into SGPRs) with 32-bit per-lane byte offsets: a chunk's score rows
+  // stay within 2 GiB, and no 64-bit address arithmetic occupies VGPRs.  The resource
+  // sizes cover exactly this workgroup's tile rows and pools below p_end.
+  const uint32_t my_row = (uint32_t)(row0 + min(wr0 + lg, nrows - 1) - chunk_row0);
+  const uint32_t orow_off = my_row * (uint32_t)ld * 4u;
+  const uint32_t grow_off = my_row * (uint32_t)ldg * 4u;
+  const uint32_t tile_end = __builtin_amdgcn_readfirstlane((uint32_t)(row0 + nrows - chunk_row0));
+  auto uni_ptr = [](const void *p) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return (void *)(((uint64_t)hi << 32) | lo);
+  };
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+  const __amdgpu_buffer_rsrc_t rs_out = __builtin_amdgcn_make_buffer_rsrc(
+      uni_ptr(out), 0, (int)__builtin_amdgcn_readfirstlane(tile_end * (uint32_t)ld * 4u), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_gmax = __builtin_amdgcn_make_buffer_rsrc(
+      uni_ptr(gmax), 0, (int)__builtin_amdgcn_readfirstlane(tile_end * (uint32_t)ldg * 4u), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc(
+      uni_ptr(kps), 0, (int)__builtin_amdgcn_readfirstlane((uint32_t)p_end * D * 2u), kRsrcWord3);
+#endif
 
   // ---- pooled-key stages through LDS ---------------------------------------
-  // Keys go global -> LDS with direct DMA loads (global_load_lds_dwordx4): one wave
+  // Keys go global -> LDS with direct DMA loads (buffer_load_dwordx4 ... lds): one wave
   // instruction fills one contiguous 1 KiB region, lane i writing bytes [16i, 16i+16).
   // Within a key row, 16-byte slot j holds chunk j ^ swz(pool) of the key, swz(pool) =
   // (pool / 4) mod NSLOT: an XOR swizzle that puts the B-fragment reads of one sub-tile
@@ -156,11 +177,11 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
       if (wave + i * kWaves < S::NREG) {  // wave-uniform
         const int pool = min(stage_base + dma_pool[i], p_end - 1);
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
-        __builtin_amdgcn_global_load_lds(
-            kps + (int64_t)pool * D + dma_off[i],
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs_kp,
             (__attribute__((address_space(3))) void *)(lds + buf * S::STAGE_BYTES +
                                                        (wave + i * kWaves) * 1024),
-            16, 0, 0);
+            16, (uint32_t)(pool * D + dma_off[i]) * 2u, 0, 0, 0);
 #else
         (void)pool;
         (void)kps;
@@ -193,8 +214,15 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   auto flush = [&]() {
     const int p0 = st_base + 4 * lc;
     if (p0 >= 0 && p0 < store_lim) {
-      *reinterpret_cast<float4 *>(orow + p0) = make_float4(vals[0], vals[1], vals[2], vals[3]);
-      if ((lc & 3) == 0) grow_max[p0 / kSub] = gval;
+#if defined(__HIP_DEVICE_COMPILE__)
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 v = {__float_as_uint(vals[0]), __float_as_uint(vals[1]), __float_as_uint(vals[2]),
+                       __float_as_uint(vals[3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs_out, orow_off + 4u * (uint32_t)p0, 0, 0);
+      if ((lc & 3) == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gval), rs_gmax,
+                                              grow_off + 4u * (uint32_t)(p0 / kSub), 0, 0);
+#endif
     }
   };
 
@@ -260,7 +288,11 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
     gval = m;
     st_base = stage_base;
-    __syncthreads();  // also waits for this wave's DMA of the next stage
+    // This wave's key DMA for the next stage must have landed before the barrier
+    // releases the other waves to read it: the barrier's fence does not cover LDS DMA,
+    // so wait on vmcnt explicitly (vmcnt(0), no other counter).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
   }
   flush();
 }
