@@ -110,6 +110,26 @@ def test_tiny_shapes_variants(variant):
         _full_check(synth.workload("tiny", T=300, budget=budget), r, res, where=f"{variant} b{budget}")
 
 
+def test_many_short_sequences_and_odd_pool_sizes():
+    """More than 32 sequences in one chunk (the score launch splits its segment list),
+    empty and one-token sequences, and pool sizes 2, 3 and 5 through the whole path."""
+    wl, r = _inputs("sq4096", 12, T=3000)
+    rng = np.random.default_rng(12)
+    lens = rng.integers(0, 70, size=80)
+    lens[::9] = 0
+    lens[1::9] = 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu = cu[cu <= 3000]
+    if cu[-1] < 3000:
+        cu = np.concatenate([cu, [3000]]).astype(np.int32)
+    r["cu_seqlens"] = cu
+    assert len(cu) - 1 > 64
+    for kpool, budget in ((2, 9), (3, 5), (5, 3)):
+        res = run_gpu(r, kpool, budget)
+        _full_check(synth.workload("sq4096", T=3000, kpool=kpool, budget=budget), r, res,
+                    where=f"many seqs kpool {kpool}")
+
+
 @pytest.mark.parametrize("name", ["sq4096", "sq4096_k1"])
 def test_sq4096_workload(name):
     wl, r = _inputs(name, 0)
