@@ -124,7 +124,10 @@ int kpool_set_overlap(int on);
  *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.
  *   scores_out NULLABLE fp32 [q_hi - q_lo, max_pools]: the fp32 scores the
  *            selection ranked, -inf where the pool is not visible.
- * Supported (H, D): (4, 16) and (32, 128).  q_lo == q_hi is a no-op. */
+ * Supported (H, D): (4, 16) and (32, 128).  q_lo == q_hi is a no-op.
+ * Sizes: one sequence's pooled keys must stay below 4 GiB (fewer than 2^24 pools
+ * at D = 128) and one fp32 score row within 2 GiB; larger returns
+ * KPOOL_EUNSUPPORTED. */
 int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
                      const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                      int32_t nseq, int32_t H, int32_t D, int32_t kpool, float scale,

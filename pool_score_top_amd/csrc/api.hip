@@ -209,6 +209,12 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
   std::vector<int32_t> cu_pools(nseq + 1);
   int32_t max_pools = 0;
   kpool_count_pools(cu_seqlens_host, nseq, kpool, cu_pools.data(), &max_pools);
+  // The score kernel addresses one sequence's pooled keys and one chunk's score rows
+  // with 32-bit byte offsets: a sequence's keys must stay below 4 GiB (16M pools at
+  // D = 128) and one score row within the 2 GiB chunk cap.
+  if ((int64_t)max_pools * D * 2 > (int64_t)0xFFFFFFFF || pitch_of(max_pools) * 4 > kChunkCapBytes)
+    return fail(KPOOL_EUNSUPPORTED, "%s: a sequence of %d pools is beyond the supported size", fn,
+                max_pools);
   const int64_t ld = pitch_of(max_pools);
   const int64_t ldg = ld / kpool::kGroup;
   const int64_t row_bytes = ws_row_bytes(ld);

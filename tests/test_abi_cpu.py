@@ -90,6 +90,8 @@ def _call_score(**kw):
     (dict(cu=[1, 64]), K.KPOOL_EINVAL),
     (dict(cu=[0, 40, 30, 64]), K.KPOOL_EINVAL),
     (dict(nseq=0), K.KPOOL_EINVAL),
+    # one sequence whose pooled keys exceed the kernel's 32-bit byte offsets (2^24 pools at D=128)
+    (dict(cu=[0, 1 << 24], kpool=1, H=32, D=128), K.KPOOL_EUNSUPPORTED),
 ])
 def test_score_topk_rejects_bad_arguments(kw, code):
     rc = _call_score(**kw)
