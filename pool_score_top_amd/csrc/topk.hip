@@ -42,6 +42,7 @@ namespace kpool {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // order_key(-inf)
 constexpr int kWavesT = kThreads / 64;
 constexpr int kRound = 8;        // group maxima loaded per thread before use
 constexpr int kPieces = 4;       // 16-byte score pieces loaded per thread before use
@@ -321,10 +322,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
           v[j] = grow[min(gb + tid + (int64_t)j * kThreads, ng - 1)];
+        // A group max must not exceed the best key actually in its group.  The score
+        // kernel's max skips NaN (key 0), so a group of NaNs reports -inf: count it
+        // as key 0 here.  (Pass 2 keeps -inf, an upper bound for such a group.)
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
-          if (gb + tid + (int64_t)j * kThreads < ng)
-            tmax[j % NMAX] = max(tmax[j % NMAX], order_key(v[j]));
+          if (gb + tid + (int64_t)j * kThreads < ng) {
+            const uint32_t k = order_key(v[j]);
+            tmax[j % NMAX] = max(tmax[j % NMAX], k == kNegInfKey ? 0u : k);
+          }
       }
     } else {
       // float4 pieces, NP per thread per step; element e of piece q goes to maximum
