@@ -121,7 +121,8 @@ int kpool_set_overlap(int on);
  *            on return.
  *   pool_ids int32 [q_hi - q_lo, budget] output: sequence-local pool ids,
  *            best first by (score desc, pool asc), -1 after the visible pools
- *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.
+ *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.  q, kp and
+ *            w must be finite (the score's ReLU does not propagate NaN).
  *   scores_out NULLABLE fp32 [q_hi - q_lo, max_pools]: the fp32 scores the
  *            selection ranked, -inf where the pool is not visible.
  * Supported (H, D): (4, 16) and (32, 128).  q_lo == q_hi is a no-op.
