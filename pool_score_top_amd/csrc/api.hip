@@ -42,7 +42,10 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t kChunkCapBytes = int64_t(1) << 31;  // 2 GiB of fp32 scores per chunk
 #ifndef KPOOL_POOL_SEG_MAX
-#define KPOOL_POOL_SEG_MAX 4096
+#define KPOOL_POOL_SEG_MAX 16384
+#endif
+#ifndef KPOOL_SCORE_TARGET_WGS
+#define KPOOL_SCORE_TARGET_WGS 1024
 #endif
 constexpr int kPoolSegMax = KPOOL_POOL_SEG_MAX;  // pools per score workgroup (max, multiple of 64)
 
@@ -265,8 +268,10 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
         max_npv = std::max<int32_t>(max_npv, (sg.hi - 1 - sg.start) / kpool + 1);
       }
       L.tile_start[L.nseg] = ntiles;
-      // pool segments per tile: enough workgroups to fill the chip, at most kPoolSegMax pools each
-      const int64_t want_segs = std::max<int64_t>(1, (1024 + ntiles - 1) / ntiles);
+      // pool segments per tile: about KPOOL_SCORE_TARGET_WGS workgroups per launch (4 per
+      // CU), at most kPoolSegMax pools each; fewer, longer workgroups reload q less often
+      const int64_t want_segs =
+          std::max<int64_t>(1, (KPOOL_SCORE_TARGET_WGS + ntiles - 1) / ntiles);
       int64_t pseg = (max_npv + want_segs - 1) / want_segs;
       pseg = std::min<int64_t>(kPoolSegMax, std::max<int64_t>(64, (pseg + 63) / 64 * 64));
       const int32_t npseg = (int32_t)((max_npv + pseg - 1) / pseg);
