@@ -133,11 +133,12 @@ def score_traffic(workload: str):
 
     The summary (profiles/score_kernel_sq524288_traffic.md) holds FETCH_SIZE and
     WRITE_SIZE per launch, scaled by a plain-copy calibration, and the sha256 of
-    score.hip it was measured on; a changed kernel makes the figure stale (None).
+    score.hip and of api.hip (which sizes the launches) it was measured on; a
+    changed kernel or launch plan makes the figure stale (None).
     """
     import hashlib
     prof = os.path.join(ROOT, "profiles", f"score_kernel_{workload}_traffic.md")
-    src = os.path.join(ROOT, "pool_score_top_amd", "csrc", "score.hip")
+    csrc = os.path.join(ROOT, "pool_score_top_amd", "csrc")
     if not os.path.exists(prof):
         return None
     vals = {}
@@ -145,9 +146,10 @@ def score_traffic(workload: str):
         if ":" in line and line.strip().startswith("score_"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if vals.get("score_hip_sha256") != sha:
-        return None
+    for key, name in (("score_hip_sha256", "score.hip"), ("score_api_hip_sha256", "api.hip")):
+        sha = hashlib.sha256(open(os.path.join(csrc, name), "rb").read()).hexdigest()
+        if vals.get(key) != sha:
+            return None
     return {"fetch": float(vals["score_fetch_bytes_per_launch"]),
             "write": float(vals["score_write_bytes_per_launch"])}
 
