@@ -189,16 +189,23 @@ struct Smem {
   int32_t done;
 };
 
-// Wave-aggregated append: lanes with c (0..4) items reserve c consecutive slots of
-// *counter with one LDS atomic per wave; returns this lane's first slot.
+// Wave-aggregated append: lanes with c (0 .. 2^BITS - 1) items reserve c consecutive
+// slots of *counter with one LDS atomic per wave; returns this lane's first slot.
+template <int BITS>
 __device__ inline uint32_t wave_reserve(uint32_t c, uint32_t *counter, int lane) {
-  const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
-  const uint32_t tot = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
+  uint64_t b[BITS];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) {
+    b[i] = __ballot(c & (1u << i));
+    tot += (uint32_t)__popcll(b[i]) << i;
+  }
   if (tot == 0) return 0;
-  const uint32_t pre =
-      __builtin_amdgcn_mbcnt_hi((uint32_t)(b0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b0, 0u)) +
-      2u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b1, 0u)) +
-      4u * __builtin_amdgcn_mbcnt_hi((uint32_t)(b2 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b2, 0u));
+  uint32_t pre = 0;
+#pragma unroll
+  for (int i = 0; i < BITS; ++i)
+    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(b[i] >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)b[i], 0u)) << i;
   uint32_t base = 0;
   if (lane == 0) base = atomicAdd(counter, tot);
   return __shfl(base, 0) + pre;
@@ -256,7 +263,7 @@ __device__ inline void append_piece(const float4 x, int64_t base, int64_t n, uin
     sel[e] = (base + e < n) && keys[e] >= bound;
     c += sel[e] ? 1u : 0u;
   }
-  uint32_t pos = wave_reserve(c, &sm.count, lane);
+  uint32_t pos = wave_reserve<3>(c, &sm.count, lane);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (sel[e]) {
@@ -376,12 +383,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
 #pragma unroll
       for (int j = 0; j < kRound; ++j)
         v[j] = grow[min(gb + tid + (int64_t)j * kThreads, ng - 1)];
+      uint32_t selm = 0, c = 0;
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
         const int64_t g = gb + tid + (int64_t)j * kThreads;
         const bool sel = g < ng && order_key(v[j]) >= bound;
-        const uint32_t pos = wave_reserve(sel ? 1u : 0u, &sm.gcount, lane);
-        if (sel && pos < (uint32_t)kGroupCap) sm.glist[pos] = (uint32_t)g;
+        selm |= sel ? (1u << j) : 0u;
+        c += sel ? 1u : 0u;
+      }
+      uint32_t pos = wave_reserve<4>(c, &sm.gcount, lane);
+#pragma unroll
+      for (int j = 0; j < kRound; ++j) {
+        if (selm & (1u << j)) {
+          if (pos < (uint32_t)kGroupCap) sm.glist[pos] = (uint32_t)(gb + tid + (int64_t)j * kThreads);
+          ++pos;
+        }
       }
     }
     __syncthreads();
@@ -461,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
           c += sel[e] ? 1u : 0u;
         }
       }
-      uint32_t pos = wave_reserve(c, &sm.count, lane);
+      uint32_t pos = wave_reserve<3>(c, &sm.count, lane);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (sel[e]) {
@@ -506,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
       const uint32_t i = i0 + tid;
       const uint64_t ck = i < count ? sm.cand[i] : 0ull;
       const bool take = i < count && (ck >> (64 - pbits)) >= prefix;
-      const uint32_t pos = wave_reserve(take ? 1u : 0u, &sm.scount, lane);
+      const uint32_t pos = wave_reserve<1>(take ? 1u : 0u, &sm.scount, lane);
       if (take) sel[pos] = ck;
     }
     __syncthreads();
