@@ -41,11 +41,26 @@
 namespace kpool {
 namespace {
 
-constexpr int kThreads = 512;
 constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // order_key(-inf)
-constexpr int kWavesT = kThreads / 64;
-constexpr int kRound = 8;        // group maxima loaded per thread before use
-constexpr int kPieces = 4;       // 16-byte score pieces loaded per thread before use
+
+// Two instances, by the number of maxima per thread (NMAX):
+//   NMAX 4: 256 threads, 1024 maxima, budgets up to 512;
+//   NMAX 8: 512 threads, 4096 maxima, budgets up to 2048.
+// Either way a wave's bound is at most its median maximum, so at most about ln 2 x
+// (number of maxima) candidates are expected (plus the spread of the minimum over
+// waves); the lists hold 8 keys per thread (2048 or 4096).  The small instance needs 25 KB of LDS, so six rows share a CU.  Each round
+// issues kRound group-max or kPieces score loads per thread, so that a row takes the
+// same number of dependent memory round trips at either workgroup size.
+template <int NMAX>
+struct Cfg {
+  static_assert(NMAX == 4 || NMAX == 8, "maxima per thread");
+  static constexpr int kThreads = NMAX == 4 ? 256 : 512;
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kRound = 4096 / kThreads;   // group maxima per thread per round
+  static constexpr int kPieces = 2048 / kThreads;  // 16-byte score pieces per thread per round
+  static constexpr int kCand = 8 * kThreads;  // candidate keys held in LDS
+  static constexpr int kGroups = kCand;       // candidate 16-pool groups
+};
 
 __device__ inline uint64_t compose(uint32_t okey, uint32_t idx) {
   return ((uint64_t)okey << 32) | (uint64_t)(~idx);
@@ -96,7 +111,7 @@ __device__ inline void wave_sort_desc(uint32_t (&x)[NMAX], int lane) {
 // ones go through LDS (buf: kThreads*M keys, laid out m-major so that every LDS access
 // of a wave is to consecutive keys).  Small distances are the most frequent stages of a
 // bitonic sort, so most of them cost no communication.
-template <int M>
+template <int M, int kThreads>
 __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
   constexpr int N = kThreads * M;
   const int e0 = tid * M;
@@ -149,7 +164,7 @@ __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
   }
 }
 
-template <int M>
+template <int M, int kThreads>
 __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32_t *orow, int tid) {
   uint64_t v[M];
   // the starting order is free: read the list m-major (consecutive keys per wave access)
@@ -158,7 +173,7 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
     const uint32_t i = m * kThreads + tid;
     v[m] = i < count ? cand[i] : 0ull;  // 0 is below every real key
   }
-  block_sort_desc<M>(v, cand, tid);
+  block_sort_desc<M, kThreads>(v, cand, tid);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int i = tid * M + m;
@@ -166,20 +181,12 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
   }
 }
 
-// LDS lists sized for NMAX maxima per thread: about 0.7 x 512 x NMAX candidates are
-// expected, so the caps leave room for the spread.
-template <int NMAX>
-struct Caps {
-  static constexpr int kCand = NMAX <= 2 ? 2048 : 4096;  // candidate keys
-  static constexpr int kGroups = kCand;                   // candidate 16-pool groups
-};
-
 template <int NMAX>
 struct Smem {
-  uint64_t cand[Caps<NMAX>::kCand];
-  uint32_t glist[Caps<NMAX>::kGroups];
+  uint64_t cand[Cfg<NMAX>::kCand];
+  uint32_t glist[Cfg<NMAX>::kGroups];
   uint32_t hist[256];
-  uint32_t wave_bound[kWavesT];
+  uint32_t wave_bound[Cfg<NMAX>::kWaves];
   uint64_t prefix;
   uint32_t count;
   uint32_t gcount;
@@ -252,7 +259,7 @@ __device__ inline void next_digit(SM &sm, uint64_t prefix, int pbits, int krem, 
 template <int NMAX>
 __device__ inline void append_piece(const float4 x, int64_t base, int64_t n, uint32_t bound,
                                     Smem<NMAX> &sm, int lane) {
-  constexpr int kCandCap = Caps<NMAX>::kCand;
+  constexpr int kCandCap = Cfg<NMAX>::kCand;
   const float xs[4] = {x.x, x.y, x.z, x.w};
   uint32_t keys[4];
   bool sel[4];
@@ -277,16 +284,20 @@ __device__ inline void append_piece(const float4 x, int64_t base, int64_t n, uin
 // ldg).  For long rows the bound then comes from the group maxima, and only the
 // groups whose max reaches it are read.
 template <bool GMAX, int NMAX>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
+__global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                         const int32_t *__restrict__ n_valid,
                                                         const int32_t *__restrict__ cu_seqlens,
                                                         int nseq, int64_t grow0, int kpool,
                                                         int budget, int32_t *__restrict__ out,
                                                         const float *__restrict__ gmax,
                                                         int64_t ldg) {
-  constexpr int kCandCap = Caps<NMAX>::kCand;
-  constexpr int kGroupCap = Caps<NMAX>::kGroups;
-  static_assert(NMAX == 2 || (NMAX % 4 == 0 && kRound % NMAX == 0), "maxima per thread");
+  constexpr int kThreads = Cfg<NMAX>::kThreads;
+  constexpr int kWavesT = Cfg<NMAX>::kWaves;
+  constexpr int kRound = Cfg<NMAX>::kRound;
+  constexpr int kPieces = Cfg<NMAX>::kPieces;
+  constexpr int kCandCap = Cfg<NMAX>::kCand;
+  constexpr int kGroupCap = Cfg<NMAX>::kGroups;
+  static_assert(kRound % NMAX == 0, "group maxima per round");
   __shared__ Smem<NMAX> sm;
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -340,9 +351,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
           }
       }
     } else {
-      // float4 pieces, NP per thread per step; element e of piece q goes to maximum
-      // (4q + e) * NMAX / (4 NP): 2 maxima share a piece, or 4 pieces feed 8 maxima
-      constexpr int NP = NMAX <= 4 ? 1 : NMAX / 4;
+      // NMAX/4 float4 pieces per thread per step; element e of piece q goes to
+      // maximum 4q + e
+      constexpr int NP = NMAX / 4;
       for (int64_t wbase = (int64_t)wave * 256 * NP; wbase < n; wbase += (int64_t)kThreads * 4 * NP) {
 #pragma unroll
         for (int q = 0; q < NP; ++q) {
@@ -351,11 +362,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
             const float4 x = *reinterpret_cast<const float4 *>(row + base);
             const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              constexpr int kDiv = 4 * NP / NMAX;
-              const int m = (4 * q + e) / (kDiv > 0 ? kDiv : 1);
-              if (base + e < n) tmax[m] = max(tmax[m], order_key(xs[e]));
-            }
+            for (int e = 0; e < 4; ++e)
+              if (base + e < n) tmax[4 * q + e] = max(tmax[4 * q + e], order_key(xs[e]));
           }
         }
       }
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
         selm |= sel ? (1u << j) : 0u;
         c += sel ? 1u : 0u;
       }
-      uint32_t pos = wave_reserve<4>(c, &sm.gcount, lane);
+      uint32_t pos = wave_reserve<(kRound >= 16 ? 5 : 4)>(c, &sm.gcount, lane);
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
         if (selm & (1u << j)) {
@@ -532,11 +540,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float *__restrict_
 
   // the sort must also cover every output slot (missing ones are written as -1)
   const uint32_t span = max(count, (uint32_t)budget);
-  if (span <= (uint32_t)kThreads) sort_and_write<1>(list, count, budget, orow, tid);
-  else if (span <= 2u * kThreads) sort_and_write<2>(list, count, budget, orow, tid);
-  else if (kCandCap <= 4 * kThreads || span <= 4u * kThreads)
-    sort_and_write<4>(list, count, budget, orow, tid);
-  else sort_and_write<(kCandCap > 4 * kThreads ? 8 : 4)>(list, count, budget, orow, tid);
+  if (span <= (uint32_t)kThreads) sort_and_write<1, kThreads>(list, count, budget, orow, tid);
+  else if (span <= 2u * kThreads) sort_and_write<2, kThreads>(list, count, budget, orow, tid);
+  else if (span <= 4u * kThreads) sort_and_write<4, kThreads>(list, count, budget, orow, tid);
+  else sort_and_write<8, kThreads>(list, count, budget, orow, tid);
 }
 
 // scores_out rows: the chunk buffer's visible scores, -inf elsewhere
@@ -555,26 +562,36 @@ __global__ __launch_bounds__(256) void scores_copy_kernel(const float *__restric
 
 }  // namespace
 
+template <bool GMAX, int NMAX>
+static void launch_topk_inst(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
+                             const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
+                             int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL((topk_kernel<GMAX, NMAX>), dim3((unsigned)nrows), dim3(Cfg<NMAX>::kThreads), 0,
+                     stream, scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax,
+                     ldg);
+}
+
 hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
                        const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
                        int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
                        hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
   if (budget > kTopkMaxBudget) return hipErrorInvalidValue;
-  // budgets above 1024 need more maxima per thread for a tight bound (and longer lists)
-  const bool big = budget > 1024;
+  // budgets above 512 need more maxima per thread for a tight bound (and longer lists)
+  const bool big = budget > 512;
   if (gmax && big)
-    hipLaunchKernelGGL((topk_kernel<true, 8>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
-                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+    launch_topk_inst<true, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, budget,
+                              out, gmax, ldg, stream);
   else if (gmax)
-    hipLaunchKernelGGL((topk_kernel<true, 2>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
-                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+    launch_topk_inst<true, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool,
+                                       budget, out, gmax, ldg, stream);
   else if (big)
-    hipLaunchKernelGGL((topk_kernel<false, 8>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
-                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+    launch_topk_inst<false, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, budget,
+                               out, gmax, ldg, stream);
   else
-    hipLaunchKernelGGL((topk_kernel<false, 2>), dim3((unsigned)nrows), dim3(kThreads), 0, stream,
-                       scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax, ldg);
+    launch_topk_inst<false, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool,
+                                        budget, out, gmax, ldg, stream);
   return hipGetLastError();
 }
 
