@@ -19,9 +19,9 @@
 //     through double-buffered LDS (one barrier per stage), so each pooled key
 //     fetched from L2 feeds 32 rows x 32 heads of MFMA work.
 //   * Causal skipping: a tile only visits pools visible to its last row.  Each
-//     row's scores are stored in 16-byte pieces up to its own visible count (the
-//     last piece may run past it; the selection reads each row only up to its
-//     visible count).
+//     row's scores are stored exactly over its own visible pools.
+//   * The ReLU / weight epilogue of one MFMA chain (row, 16-head block) runs on the
+//     VALU while the next chains' MFMAs run, so the two pipes overlap.
 //   * The head dim is split across the 4 lane groups as contiguous runs of
 //     D/4 (a fixed permutation of K applied to q and kp alike), so every lane
 //     reads 16-byte contiguous pieces.
@@ -39,6 +39,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+#ifndef KPOOL_SCORE_SCHED
+#define KPOOL_SCORE_SCHED 1
+#endif
 #ifndef KPOOL_SCORE_WAVES
 #define KPOOL_SCORE_WAVES 8
 #endif
@@ -166,28 +169,25 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // scores are finite and never read), and chunks past D (padding of the K step) meet
   // zero q fragments, so duplicates are harmless.
   auto swz = [](int pool) { return (pool >> 2) & (S::NSLOT - 1); };
-  int dma_pool[S::RPW], dma_off[S::RPW];
-#pragma unroll
-  for (int i = 0; i < S::RPW; ++i) {
-    const int region = min(wave + i * kWaves, S::NREG - 1);
-    const int byte = region * 1024 + lane * 16;
-    dma_pool[i] = byte / S::ROWB;
-    const int slot = (byte % S::ROWB) / 16;
-    dma_off[i] = min((slot ^ swz(dma_pool[i])) * 8, D - 8);
-  }
+  // Lane offsets of the DMA regions are recomputed per stage from the lane id (a few
+  // VALU instructions per stage) rather than held in VGPRs across the loop.
   auto dma_stage = [&](int stage_base, int buf) {
 #pragma unroll
     for (int i = 0; i < S::RPW; ++i) {
       if (wave + i * kWaves < S::NREG) {  // wave-uniform
-        const int pool = min(stage_base + dma_pool[i], p_end - 1);
+        const int byte = (wave + i * kWaves) * 1024 + lane * 16;
+        const int pl = byte / S::ROWB;
+        const int off = min((((byte % S::ROWB) / 16) ^ swz(pl)) * 8, D - 8);
+        const int pool = min(stage_base + pl, p_end - 1);
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs_kp,
             (__attribute__((address_space(3))) void *)(lds + buf * S::STAGE_BYTES +
                                                        (wave + i * kWaves) * 1024),
-            16, (uint32_t)(pool * D + dma_off[i]) * 2u, 0, 0, 0);
+            16, (uint32_t)(pool * D + off) * 2u, 0, 0, 0);
 #else
         (void)pool;
+        (void)off;
         (void)kps;
 #endif
       }
@@ -197,108 +197,146 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   auto b_addr = [&](int pl, int c) { return pl * S::ROWB + ((c ^ swz(pl)) * 16); };
 
   // Sub-tile `sub` of a stage holds the pools 4c + sub (c = 0..15, the MFMA column), so
-  // after the 4 sub-tiles a lane owns 4 consecutive pools of its row and stores them with
-  // one 16-byte store.  A stage's scores stay in registers and are stored after the
-  // stage's barrier: stores are then issued before the next stage's key fetch, so
-  // waiting for that fetch never waits on fresh stores.
+  // the 4 sub-tiles of a stage give a lane 4 consecutive pools of its row, i.e. every
+  // 16-pool group of a row sits in one lane quad.
   constexpr int kSubs = kStagePools / kSub;
-  static_assert(kSubs == 4, "one 16-byte store per lane per stage");
+  static_assert(kSubs == 4, "a 16-pool group per lane quad and stage");
   // Every stage computes all its sub-tiles (no branches between the LDS prefetches and
-  // the MFMAs).  A lane stores its 4 pools when the first is visible to its row; pools
-  // past the row's visible count then receive finite values that the selection never
-  // reads (it reads each row only up to its visible count), and they stay inside this
-  // workgroup's 64-aligned stage, so columns of neighbouring segments are never touched.
-  // Alongside the scores, the max of every 16-pool group of a row (over its visible
-  // pools) goes to `gmax`; the selection reads those first and then only the groups
-  // that can hold a winner.
+  // the MFMAs); a lane stores a score only if its pool is visible to its row and below
+  // p_end (store_lim), so each row is written exactly over its visible pools of this
+  // segment.  Alongside the scores, the max of every 16-pool group of a row (over its
+  // visible pools) goes to `gmax`; the selection reads those first and then only the
+  // groups that can hold a winner.  Pools at or past p_end are invisible to every row
+  // of the tile, so store_lim also bounds the group max.
   const bool row_ok = wr0 + lg < nrows;
   const int store_lim = row_ok ? min(my_nvis, p_end) : 0;
-  float vals[kSubs], gval = 0.0f;
-  int st_base = -(1 << 30);  // the stage whose scores are pending in vals (none yet)
-  auto flush = [&]() {
-    const int p0 = st_base + 4 * lc;
-    if (p0 >= 0 && p0 < store_lim) {
+  // Each reduced score is stored as soon as it exists: lane (g, c) holds pool 4c + sub
+  // of its stage for row g.  The max of each 16-pool group (pools 16j .. 16j + 15 of a
+  // stage: 4 sub-tiles x lanes 4j .. 4j + 3) is kept as a running max per lane over the
+  // stage and reduced across the lane quad when the stage's last sub-tile is stored.
+  // Every store instruction is issued by every wave, lanes with nothing to store giving
+  // an offset at or past the buffer's range (the hardware range check drops such
+  // stores; the ranges are at most 2 GiB), so the number of stores a wave issues per
+  // stage is fixed; the wait for the key DMA below relies on it.
+  constexpr uint32_t kDrop = 0x80000000u;
+  float gm = -__builtin_inff();
+  auto emit = [&](float v, int base, int sub, bool live = true) {
+    const int p = base + 4 * lc + sub;
+    const bool vis = live && p < store_lim;
+    gm = fmaxf(gm, vis ? v : -__builtin_inff());
 #if defined(__HIP_DEVICE_COMPILE__)
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 v = {__float_as_uint(vals[0]), __float_as_uint(vals[1]), __float_as_uint(vals[2]),
-                       __float_as_uint(vals[3])};
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs_out, orow_off + 4u * (uint32_t)p0, 0, 0);
-      if ((lc & 3) == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gval), rs_gmax,
-                                              grow_off + 4u * (uint32_t)(p0 / kSub), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs_out,
+                                          vis ? orow_off + 4u * (uint32_t)p : kDrop, 0, 0);
 #endif
+    if (sub == kSubs - 1) {
+      float m = gm;
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+      const int p0 = base + 4 * lc;
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __float_as_uint(m), rs_gmax,
+          live && (lc & 3) == 0 && p0 < store_lim ? grow_off + 4u * (uint32_t)(p0 / kSub) : kDrop, 0, 0);
+#endif
+      gm = -__builtin_inff();
     }
+  };
+
+  // Each sub-tile's MFMAs run chain by chain: chain c = (row r, head block mb) takes its
+  // K steps back to back (the accumulator dependence is forwarded inside the matrix
+  // pipe), and while chain c runs, the VALU works on the epilogue (ReLU and head weights
+  // of its 4 outputs) of the chain two places before it, whose MFMAs have completed by
+  // then; chains 0 and 1 take the previous sub-tile's last two chains, and chain 1 then
+  // that sub-tile's head-sum reduction and store.  The epilogue thus interleaves with
+  // the MFMAs at about two VALU instructions per MFMA, and only three chains'
+  // accumulators are live.  Every row accumulates its heads in the same order
+  // (block 0, then block 1; the lane's 4 heads in order), so a score does not depend on
+  // which slot of a wave its row occupies.
+  constexpr int NCH = kRowsPerWave * S::MB;
+  float x[kRowsPerWave] = {};  // head sums in progress (this lane's heads)
+  // the two chains whose epilogues are pending (pb is the older)
+  floatx4 pa = floatx4{0.0f, 0.0f, 0.0f, 0.0f}, pb = pa;
+  auto epi = [&](int c) {
+    const int r = c / S::MB, mb = c % S::MB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(pb[i], 0.0f), sw[r][mb][i], x[r]);
+  };
+  // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
+  auto reduce = [&]() {
+    const float y01 = swap16_sum(x[0], x[1]);
+    const float y23 = swap16_sum(x[2], x[3]);
+    // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
+    auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) x[r] = 0.0f;
+    return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+  };
+  auto b_read = [&](const unsigned char *sb, int sub, int ks) {
+    return *reinterpret_cast<const bf16x8 *>(sb + b_addr(4 * lc + sub, lg * (S::KG / 8) + ks));
   };
 
   const int nstage = (p_end - p_begin + kStagePools - 1) / kStagePools;
   dma_stage(p_begin, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first stage's keys have landed
   __syncthreads();
   for (int st = 0; st < nstage; ++st) {
     const int stage_base = p_begin + st * kStagePools;
-    flush();
     if (st + 1 < nstage) dma_stage(stage_base + kStagePools, (st + 1) & 1);
     const unsigned char *sb = lds + (st & 1) * S::STAGE_BYTES;
     // B fragments are read one sub-tile ahead, so LDS latency hides behind the MFMAs.
     bf16x8 bb[2][S::KS];
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks)
-      bb[0][ks] = *reinterpret_cast<const bf16x8 *>(sb + b_addr(4 * lc, lg * (S::KG / 8) + ks));
+    for (int ks = 0; ks < S::KS; ++ks) bb[0][ks] = b_read(sb, 0, ks);
+
 #pragma unroll
     for (int sub = 0; sub < kSubs; ++sub) {
       if (sub + 1 < kSubs) {
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks)
-          bb[(sub + 1) & 1][ks] = *reinterpret_cast<const bf16x8 *>(
-              sb + b_addr(4 * lc + sub + 1, lg * (S::KG / 8) + ks));
+        for (int ks = 0; ks < S::KS; ++ks) bb[(sub + 1) & 1][ks] = b_read(sb, sub + 1, ks);
       }
       const bf16x8 (&b)[S::KS] = bb[sub & 1];
-      // all (row, M block) accumulators advance together: 8 independent MFMAs per K step
-      floatx4 acc[kRowsPerWave][S::MB];
+#if KPOOL_SCORE_SCHED
+      // the next sub-tile's B reads go out first, ahead of this sub-tile's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r)
+      for (int c = 0; c < NCH; ++c) {
+        const int r = c / S::MB, mb = c % S::MB;
+        floatx4 t = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int mb = 0; mb < S::MB; ++mb) acc[r][mb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ks = 0; ks < S::KS; ++ks) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], t, 0, 0, 0);
+        epi((c + NCH - 2) % NCH);
+        if (c == 1) {
+          // the previous sub-tile (stage st - 1's last one when sub == 0) is complete;
+          // the segment's first sub-tile has none, and its zero state is not stored
+          emit(reduce(), sub == 0 ? stage_base - kStagePools : stage_base, (sub + kSubs - 1) % kSubs,
+               sub > 0 || st > 0);
+        }
+        pb = pa;
+        pa = t;
+#if KPOOL_SCORE_SCHED
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks)
-#pragma unroll
-        for (int r = 0; r < kRowsPerWave; ++r)
-#pragma unroll
-          for (int mb = 0; mb < S::MB; ++mb)
-            acc[r][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], acc[r][mb], 0, 0, 0);
-      // epilogue: ReLU, head weights and the head sum
-      float x[kRowsPerWave];
-#pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) {
-        x[r] = 0.0f;
-#pragma unroll
-        for (int mb = 0; mb < S::MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(acc[r][mb][i], 0.0f), sw[r][mb][i], x[r]);
+        for (int ks = 0; ks < S::KS; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+        }
+#endif
       }
-      // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
-      const float y01 = swap16_sum(x[0], x[1]);
-      const float y23 = swap16_sum(x[2], x[3]);
-      // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
-      auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
-      vals[sub] = __uint_as_float(z[0]) + __uint_as_float(z[1]);
     }
-    // max of each 16-pool group over the row's visible pools: 4 own values, then the
-    // 4 lanes of the quad (pools 16j .. 16j + 15 of the stage sit in lanes 4j .. 4j + 3)
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int sub = 0; sub < kSubs; ++sub)
-      m = fmaxf(m, stage_base + 4 * lc + sub < my_nvis ? vals[sub] : -__builtin_inff());
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
-    gval = m;
-    st_base = stage_base;
     // This wave's key DMA for the next stage must have landed before the barrier
     // releases the other waves to read it: the barrier's fence does not cover LDS DMA,
-    // so wait on vmcnt explicitly (vmcnt(0), no other counter).
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // so wait on vmcnt explicitly.  Vector memory operations complete in issue order for
+    // this counter, and this stage issued at least 3 stores after the DMA (one per
+    // sub-tile from the second on), so vmcnt(3) covers the DMA without waiting for the
+    // newest stores.
+    __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3), no other counter
     __syncthreads();
   }
-  flush();
+  // drain: the last two chains' epilogues, then the last sub-tile's reduction and store
+  epi(NCH - 2);
+  pb = pa;
+  epi(NCH - 1);
+  emit(reduce(), p_begin + (nstage - 1) * kStagePools, kSubs - 1);
 }
 
 template <int H, int D>
