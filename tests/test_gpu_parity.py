@@ -323,3 +323,25 @@ def test_expand_standalone_matches_oracle():
         sub = K.expand(torch.from_numpy(ids[10:20]).cuda(), cu, torch.from_numpy(cu).cuda(), kpool,
                        budget, 10, 20).cpu().numpy()
         np.testing.assert_array_equal(sub, got[10:20])
+
+
+@pytest.mark.parametrize("kpool,budget,variant", [(4, 512, "w_zero"), (4, 512, "k_const"),
+                                                  (1, 2048, "w_zero"), (1, 2048, "k_const")])
+def test_long_rows_all_tied_take_the_exact_path(kpool, budget, variant):
+    """Rows long enough for group pruning (>= 1024 groups at budget 512, >= 4096 at
+    budget 2048) whose scores are all equal (zero weights, or identical pooled keys):
+    every group max ties with the bound, the candidate list overflows and the exact
+    radix path must return the first `budget` pools in index order (ties go to the
+    smaller pool index)."""
+    T = 70000
+    wl = synth.workload("sq4096", T=T, kpool=kpool, budget=budget, variant=variant)
+    inp = synth.device_inputs(wl, 0)
+    sel = K.Selector(inp["cu_seqlens"], kpool, budget, wl.H, wl.D)
+    out = sel.run(inp["q"], inp["k"], inp["w"])
+    ids = out["pool_ids"].cpu().numpy()
+    m = np.minimum(budget, np.arange(T) // kpool + 1)
+    col = np.arange(budget)[None, :]
+    expect = np.where(col < m[:, None], col, -1).astype(np.int32)
+    np.testing.assert_array_equal(ids, expect)
+    # the long rows did go through group pruning's overflow (not only short rows)
+    assert (T - 1) // kpool + 1 >= (16 if budget <= 512 else 64) * 1024
