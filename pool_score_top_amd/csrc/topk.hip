@@ -47,19 +47,28 @@ constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // order_key(-inf)
 //   NMAX 4: 256 threads, 1024 maxima, budgets up to 512;
 //   NMAX 8: 512 threads, 4096 maxima, budgets up to 2048.
 // Either way a wave's bound is at most its median maximum, so at most about ln 2 x
-// (number of maxima) candidates are expected (plus the spread of the minimum over
-// waves); the lists hold 8 keys per thread (2048 or 4096).  The small instance needs 25 KB of LDS, so six rows share a CU.  Each round
-// issues kRound group-max or kPieces score loads per thread, so that a row takes the
-// same number of dependent memory round trips at either workgroup size.
+// (number of maxima) candidates are expected, plus the spread of the minimum over
+// waves (iid rows of 16k-131k pools at budget 512: about 775 candidates in about 740
+// groups, at most 930 and 880 over 200 rows).  The top-k is latency-bound, so the
+// small instance is sized for rows in flight: lists of 1280 candidates and 1280
+// groups (16.4 KB of LDS) and rounds of 8 group maxima or 4 score pieces per thread
+// (52 VGPRs) let nine rows share a CU.  The large instance holds 4096 of each.  A row
+// that overflows a list takes the exact path, so the caps bound speed, not results.
 template <int NMAX>
 struct Cfg {
   static_assert(NMAX == 4 || NMAX == 8, "maxima per thread");
   static constexpr int kThreads = NMAX == 4 ? 256 : 512;
   static constexpr int kWaves = kThreads / 64;
-  static constexpr int kRound = 4096 / kThreads;   // group maxima per thread per round
-  static constexpr int kPieces = 2048 / kThreads;  // 16-byte score pieces per thread per round
-  static constexpr int kCand = 8 * kThreads;  // candidate keys held in LDS
-  static constexpr int kGroups = kCand;       // candidate 16-pool groups
+  static constexpr int kRound = 8;   // group maxima per thread per round
+  static constexpr int kPieces = 4;  // 16-byte score pieces per thread per round
+  static constexpr int kCand = NMAX == 4 ? 5 * kThreads : 8 * kThreads;  // candidate keys in LDS
+  static constexpr int kGroups = kCand;                                  // candidate 16-pool groups
+  static constexpr int kMaxBudget = NMAX == 4 ? 512 : kTopkMaxBudget;
+  // the cut gathers `budget` keys into the group list's space
+  static_assert(kGroups / 2 >= kMaxBudget, "cut buffer");
+  // a list longer than the budget's sort size is cut first, so sorts span at most
+  // max(budget, that size) <= 4 kThreads keys
+  static_assert(kMaxBudget <= 4 * kThreads && 4 * kThreads <= kCand, "sort sizes");
 };
 
 __device__ inline uint64_t compose(uint32_t okey, uint32_t idx) {
@@ -399,7 +408,8 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
         selm |= sel ? (1u << j) : 0u;
         c += sel ? 1u : 0u;
       }
-      uint32_t pos = wave_reserve<(kRound >= 16 ? 5 : 4)>(c, &sm.gcount, lane);
+      static_assert(kRound < 16, "per-thread count fits 4 bits");
+      uint32_t pos = wave_reserve<4>(c, &sm.gcount, lane);
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
         if (selm & (1u << j)) {
@@ -538,12 +548,13 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     count = (uint32_t)budget;
   }
 
-  // the sort must also cover every output slot (missing ones are written as -1)
+  // The sort must also cover every output slot (missing ones are written as -1).  Its
+  // span is at most 4 kThreads: a list in a larger sort class than the budget was cut
+  // to the budget above, and budgets are at most 4 kThreads.
   const uint32_t span = max(count, (uint32_t)budget);
   if (span <= (uint32_t)kThreads) sort_and_write<1, kThreads>(list, count, budget, orow, tid);
   else if (span <= 2u * kThreads) sort_and_write<2, kThreads>(list, count, budget, orow, tid);
-  else if (span <= 4u * kThreads) sort_and_write<4, kThreads>(list, count, budget, orow, tid);
-  else sort_and_write<8, kThreads>(list, count, budget, orow, tid);
+  else sort_and_write<4, kThreads>(list, count, budget, orow, tid);
 }
 
 // scores_out rows: the chunk buffer's visible scores, -inf elsewhere
