@@ -6,38 +6,53 @@
 // payload).  Keeping a filtered slot in place as -1 and int32 token ids are
 // this library's reading.
 //
-// HBM-write-bound: one thread per (row, slot) reads one int32 and writes
-// kpool int32 (one 16-byte store when kpool == 4).
+// HBM-bound: workgroups stride over rows (one sequence lookup per row), threads over
+// a row's slots.  kpool == 4: each slot is one 16-byte store; kpool == 1 with 16-byte
+// aligned rows: 4 slots per thread through 16-byte loads and stores; otherwise one
+// token per thread and iteration.
 #include "kpool_internal.h"
 
 namespace kpool {
 namespace {
 
-__global__ __launch_bounds__(256) void expand_kernel(const int32_t *__restrict__ pool_ids,
-                                                     const int32_t *__restrict__ cu_seqlens,
-                                                     int nseq, int kpool, int64_t q_lo,
-                                                     int64_t nrows, int budget,
-                                                     int32_t *__restrict__ tok) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= nrows * budget) return;
-  const int64_t r = gid / budget;
-  const int64_t i = q_lo + r;
-  const int s = find_seq(cu_seqlens, nseq, i);
-  const int64_t t = i - cu_seqlens[s];
-  const int32_t p = pool_ids[gid];
-  int32_t *o = tok + gid * kpool;
-  if (kpool == 4) {
-    int32_t v[4];
+constexpr int kExpandThreads = 256;
+constexpr int kExpandMaxBlocks = 65536;
+
+__global__ __launch_bounds__(kExpandThreads) void expand_kernel(const int32_t *__restrict__ pool_ids,
+                                                                const int32_t *__restrict__ cu_seqlens,
+                                                                int nseq, int kpool, int64_t q_lo,
+                                                                int64_t nrows, int budget, bool vec,
+                                                                int32_t *__restrict__ tok) {
+  for (int64_t r = blockIdx.x; r < nrows; r += gridDim.x) {
+    const int64_t i = q_lo + r;
+    const int s = find_seq(cu_seqlens, nseq, i);
+    const int64_t t = i - cu_seqlens[s];
+    const int32_t *prow = pool_ids + r * budget;
+    int32_t *orow = tok + r * budget * kpool;
+    if (kpool == 4) {
+      for (int j = threadIdx.x; j < budget; j += kExpandThreads) {
+        const int32_t p = prow[j];
+        int32_t v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t tk = (int64_t)p * 4 + j;
-      v[j] = (p >= 0 && tk <= t) ? (int32_t)tk : -1;
-    }
-    *reinterpret_cast<int4 *>(o) = make_int4(v[0], v[1], v[2], v[3]);
-  } else {
-    for (int j = 0; j < kpool; ++j) {
-      const int64_t tk = (int64_t)p * kpool + j;
-      o[j] = (p >= 0 && tk <= t) ? (int32_t)tk : -1;
+        for (int k = 0; k < 4; ++k) {
+          const int64_t tk = (int64_t)p * 4 + k;
+          v[k] = (p >= 0 && tk <= t) ? (int32_t)tk : -1;
+        }
+        *reinterpret_cast<int4 *>(orow + 4 * j) = make_int4(v[0], v[1], v[2], v[3]);
+      }
+    } else if (kpool == 1 && vec) {
+      for (int j = threadIdx.x; j < budget / 4; j += kExpandThreads) {
+        const int4 p = reinterpret_cast<const int4 *>(prow)[j];
+        auto f = [&](int32_t q) { return (q >= 0 && q <= t) ? q : -1; };
+        reinterpret_cast<int4 *>(orow)[j] = make_int4(f(p.x), f(p.y), f(p.z), f(p.w));
+      }
+    } else {
+      const int64_t n = (int64_t)budget * kpool;
+      for (int64_t e = threadIdx.x; e < n; e += kExpandThreads) {
+        const int32_t p = prow[e / kpool];
+        const int64_t tk = (int64_t)p * kpool + e % kpool;
+        orow[e] = (p >= 0 && tk <= t) ? (int32_t)tk : -1;
+      }
     }
   }
 }
@@ -47,11 +62,11 @@ __global__ __launch_bounds__(256) void expand_kernel(const int32_t *__restrict__
 hipError_t launch_expand(const int32_t *pool_ids, const int32_t *cu_seqlens, int32_t nseq,
                          int32_t kpool, int64_t q_lo, int64_t nrows, int32_t budget,
                          int32_t *token_ids, hipStream_t stream) {
-  const int64_t n = nrows * budget;
-  if (n <= 0) return hipSuccess;
-  const int block = 256;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)((n + block - 1) / block)), dim3(block), 0,
-                     stream, pool_ids, cu_seqlens, nseq, kpool, q_lo, nrows, budget, token_ids);
+  if (nrows <= 0) return hipSuccess;
+  const bool vec = budget % 4 == 0 && ((uintptr_t)pool_ids % 16) == 0 && ((uintptr_t)token_ids % 16) == 0;
+  const unsigned blocks = (unsigned)(nrows < kExpandMaxBlocks ? nrows : kExpandMaxBlocks);
+  hipLaunchKernelGGL(expand_kernel, dim3(blocks), dim3(kExpandThreads), 0, stream, pool_ids,
+                     cu_seqlens, nseq, kpool, q_lo, nrows, budget, vec, token_ids);
   return hipGetLastError();
 }
 
