@@ -19,7 +19,9 @@
 //     through double-buffered LDS (one barrier per stage), so each pooled key
 //     fetched from L2 feeds 32 rows x 32 heads of MFMA work.
 //   * Causal skipping: a tile only visits pools visible to its last row.  Each
-//     row's scores are stored exactly over its own visible pools.
+//     row's scores are stored in 16-byte pieces up to its own visible count (the
+//     last piece may run past it; the selection reads each row only up to its
+//     visible count).
 //   * The ReLU / weight epilogue of one MFMA chain (row, 16-head block) runs on the
 //     VALU while the next chains' MFMAs run, so the two pipes overlap.
 //   * The head dim is split across the 4 lane groups as contiguous runs of
@@ -197,49 +199,47 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   auto b_addr = [&](int pl, int c) { return pl * S::ROWB + ((c ^ swz(pl)) * 16); };
 
   // Sub-tile `sub` of a stage holds the pools 4c + sub (c = 0..15, the MFMA column), so
-  // the 4 sub-tiles of a stage give a lane 4 consecutive pools of its row, i.e. every
-  // 16-pool group of a row sits in one lane quad.
+  // the 4 sub-tiles of a stage give a lane 4 consecutive pools of its row (one 16-byte
+  // store), and every 16-pool group of a row sits in one lane quad.
   constexpr int kSubs = kStagePools / kSub;
-  static_assert(kSubs == 4, "a 16-pool group per lane quad and stage");
+  static_assert(kSubs == 4, "one 16-byte store per lane per stage");
   // Every stage computes all its sub-tiles (no branches between the LDS prefetches and
-  // the MFMAs); a lane stores a score only if its pool is visible to its row and below
-  // p_end (store_lim), so each row is written exactly over its visible pools of this
-  // segment.  Alongside the scores, the max of every 16-pool group of a row (over its
-  // visible pools) goes to `gmax`; the selection reads those first and then only the
-  // groups that can hold a winner.  Pools at or past p_end are invisible to every row
-  // of the tile, so store_lim also bounds the group max.
+  // the MFMAs).  Alongside the scores, the max of every 16-pool group of a row (over
+  // its visible pools) goes to `gmax`; the selection reads those first and then only
+  // the groups that can hold a winner.  Pools at or past p_end are invisible to every
+  // row of the tile, so store_lim (visible and below p_end) bounds both stores.
   const bool row_ok = wr0 + lg < nrows;
   const int store_lim = row_ok ? min(my_nvis, p_end) : 0;
-  // Each reduced score is stored as soon as it exists: lane (g, c) holds pool 4c + sub
-  // of its stage for row g.  The max of each 16-pool group (pools 16j .. 16j + 15 of a
-  // stage: 4 sub-tiles x lanes 4j .. 4j + 3) is kept as a running max per lane over the
-  // stage and reduced across the lane quad when the stage's last sub-tile is stored.
-  // Every store instruction is issued by every wave, lanes with nothing to store giving
-  // an offset at or past the buffer's range (the hardware range check drops such
-  // stores; the ranges are at most 2 GiB), so the number of stores a wave issues per
-  // stage is fixed; the wait for the key DMA below relies on it.
+  // A stage's reduced scores stay in registers (lane (g, c) holds pools 4c .. 4c + 3 of
+  // row g) until its last sub-tile is reduced, then go out with one 16-byte store per
+  // lane, so every score row is written in whole 256-byte runs.  A lane stores when its
+  // first pool is visible to its row; up to 3 pools past the row's visible count then
+  // receive finite values that the selection never reads (it reads each row only up to
+  // its visible count), inside this workgroup's 64-aligned stage and the row's pitch.
+  // The max of each 16-pool group (over the row's visible pools) is formed from the
+  // same 4 values plus 2 quad steps.  Both stores are issued by every wave, lanes with
+  // nothing to store giving an offset at or past the buffer's range (the hardware range
+  // check drops such stores; the ranges are at most 2 GiB), so a wave issues exactly 2
+  // stores per stage; the wait for the key DMA below relies on it.
   constexpr uint32_t kDrop = 0x80000000u;
-  float gm = -__builtin_inff();
-  auto emit = [&](float v, int base, int sub, bool live = true) {
-    const int p = base + 4 * lc + sub;
-    const bool vis = live && p < store_lim;
-    gm = fmaxf(gm, vis ? v : -__builtin_inff());
+  float vals[kSubs] = {};
+  auto flush = [&](int base, bool live) {
+    const int p0 = base + 4 * lc;
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int sub = 0; sub < kSubs; ++sub) m = fmaxf(m, p0 + sub < store_lim ? vals[sub] : -__builtin_inff());
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
+    const bool vis = live && p0 < store_lim;
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs_out,
-                                          vis ? orow_off + 4u * (uint32_t)p : kDrop, 0, 0);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 u = {__float_as_uint(vals[0]), __float_as_uint(vals[1]), __float_as_uint(vals[2]),
+                     __float_as_uint(vals[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(u, rs_out, vis ? orow_off + 4u * (uint32_t)p0 : kDrop, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs_gmax,
+                                          vis && (lc & 3) == 0 ? grow_off + 4u * (uint32_t)(p0 / kSub) : kDrop,
+                                          0, 0);
 #endif
-    if (sub == kSubs - 1) {
-      float m = gm;
-      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
-      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
-      const int p0 = base + 4 * lc;
-#if defined(__HIP_DEVICE_COMPILE__)
-      __builtin_amdgcn_raw_buffer_store_b32(
-          __float_as_uint(m), rs_gmax,
-          live && (lc & 3) == 0 && p0 < store_lim ? grow_off + 4u * (uint32_t)(p0 / kSub) : kDrop, 0, 0);
-#endif
-      gm = -__builtin_inff();
-    }
   };
 
   // Each sub-tile's MFMAs run chain by chain: chain c = (row r, head block mb) takes its
@@ -307,10 +307,11 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
         for (int ks = 0; ks < S::KS; ++ks) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], t, 0, 0, 0);
         epi((c + NCH - 2) % NCH);
         if (c == 1) {
-          // the previous sub-tile (stage st - 1's last one when sub == 0) is complete;
-          // the segment's first sub-tile has none, and its zero state is not stored
-          emit(reduce(), sub == 0 ? stage_base - kStagePools : stage_base, (sub + kSubs - 1) % kSubs,
-               sub > 0 || st > 0);
+          // the previous sub-tile (stage st - 1's last one when sub == 0) is complete,
+          // and with it, when sub == 0, the previous stage (the segment's first
+          // sub-tile has none: its zero state is not stored)
+          vals[(sub + kSubs - 1) % kSubs] = reduce();
+          if (sub == 0) flush(stage_base - kStagePools, st > 0);
         }
         pb = pa;
         pa = t;
@@ -326,17 +327,17 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     // This wave's key DMA for the next stage must have landed before the barrier
     // releases the other waves to read it: the barrier's fence does not cover LDS DMA,
     // so wait on vmcnt explicitly.  Vector memory operations complete in issue order for
-    // this counter, and this stage issued at least 3 stores after the DMA (one per
-    // sub-tile from the second on), so vmcnt(3) covers the DMA without waiting for the
-    // newest stores.
-    __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3), no other counter
+    // this counter, and this stage issued 2 stores after the DMA (the previous stage's
+    // scores and group maxima), so vmcnt(2) covers the DMA without waiting for them.
+    __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2), no other counter
     __syncthreads();
   }
   // drain: the last two chains' epilogues, then the last sub-tile's reduction and store
   epi(NCH - 2);
   pb = pa;
   epi(NCH - 1);
-  emit(reduce(), p_begin + (nstage - 1) * kStagePools, kSubs - 1);
+  vals[kSubs - 1] = reduce();
+  flush(p_begin + (nstage - 1) * kStagePools, true);
 }
 
 template <int H, int D>
