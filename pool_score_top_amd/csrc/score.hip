@@ -41,15 +41,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-#ifndef KPOOL_SCORE_SCHED
-#define KPOOL_SCORE_SCHED 1
+// Rows per wave: 4 (8 waves, two per SIMD).  8 rows per wave (4 waves, one per SIMD,
+// halving the B-fragment reads per flop) needs the q fragments in AGPRs, which the
+// operand loads below force, and the MFMA results in VGPRs (build flag
+// -mllvm -amdgpu-mfma-vgpr-form=1); it passes the same tests and measured no faster.
+#ifndef KPOOL_SCORE_RPW
+#define KPOOL_SCORE_RPW 4
 #endif
-#ifndef KPOOL_SCORE_WAVES
-#define KPOOL_SCORE_WAVES 8
-#endif
-constexpr int kWaves = KPOOL_SCORE_WAVES;  // waves per workgroup
-constexpr int kRowsPerWave = 4;  // the 4-row swap reduction needs exactly 4
-constexpr int kTileRows = kWaves * kRowsPerWave;
+constexpr int kTileRows = 32;
+constexpr int kRowsPerWave = KPOOL_SCORE_RPW;
+static_assert(kRowsPerWave % 4 == 0, "the swap reduction sums 4 rows at a time");
+constexpr int kQuads = kRowsPerWave / 4;  // row quads per wave
+constexpr int kWaves = kTileRows / kRowsPerWave;  // waves per workgroup
 constexpr int kStagePools = 64;
 constexpr int kSub = 16;
 
@@ -63,7 +66,7 @@ struct Shape {
   static constexpr int NSLOT = DP / 8;            // 16-byte slots per key row
   static constexpr int STAGE_BYTES = kStagePools * ROWB;
   static constexpr int NREG = STAGE_BYTES / 1024; // 1 KiB DMA regions per stage (one per wave op)
-  static constexpr int RPW = (NREG + kWaves - 1) / kWaves;  // regions per wave
+  static constexpr int RGW = (NREG + kWaves - 1) / kWaves;  // regions per wave
 };
 
 // permlane16_swap(a, b) gives a' = [a.g0, b.g0, a.g2, b.g2] and b' = [a.g1, b.g1, a.g3, b.g3]
@@ -125,6 +128,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
                                                          min(kk, D - 8));
         const uint4 z = ok ? v : make_uint4(0, 0, 0, 0);
         a[r][mb][ks] = __builtin_bit_cast(bf16x8, z);
+        if (kRowsPerWave > 4) asm volatile("" : "+a"(a[r][mb][ks]));
       }
       const int h0 = mb * 16 + lg * 4;  // this lane's 4 output heads; H % 4 == 0
       const float4 wv = *reinterpret_cast<const float4 *>(w + grow * H + min(h0, H - 4));
@@ -135,15 +139,18 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
       sw[r][mb][3] = wok ? scale * wv.w : 0.0f;
     }
   }
-  // visible pools of the row this lane stores (row wr0 + lg)
-  const int my_nvis = (wr0 + lg < nrows) ? (int)((t0 + wr0 + lg) / kpool) + 1 : 0;
   // Global accesses of the loop go through buffer resources built from wave-uniform
   // values (forced into SGPRs) with 32-bit per-lane byte offsets: a chunk's score rows
   // stay within 2 GiB, and no 64-bit address arithmetic occupies VGPRs.  The resource
   // sizes cover exactly this workgroup's tile rows and pools below p_end.
-  const uint32_t my_row = (uint32_t)(row0 + min(wr0 + lg, nrows - 1) - chunk_row0);
-  const uint32_t orow_off = my_row * (uint32_t)ld * 4u;
-  const uint32_t grow_off = my_row * (uint32_t)ldg * 4u;
+  // Lane group lg stores row wr0 + 4j + lg of every row quad j.
+  uint32_t orow_off[kQuads], grow_off[kQuads];
+#pragma unroll
+  for (int j = 0; j < kQuads; ++j) {
+    const uint32_t my_row = (uint32_t)(row0 + min(wr0 + 4 * j + lg, nrows - 1) - chunk_row0);
+    orow_off[j] = my_row * (uint32_t)ld * 4u;
+    grow_off[j] = my_row * (uint32_t)ldg * 4u;
+  }
   const uint32_t tile_end = __builtin_amdgcn_readfirstlane((uint32_t)(row0 + nrows - chunk_row0));
   auto uni_ptr = [](const void *p) {
     const uint64_t a = (uint64_t)p;
@@ -175,8 +182,8 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // VALU instructions per stage) rather than held in VGPRs across the loop.
   auto dma_stage = [&](int stage_base, int buf) {
 #pragma unroll
-    for (int i = 0; i < S::RPW; ++i) {
-      if (wave + i * kWaves < S::NREG) {  // wave-uniform
+    for (int i = 0; i < S::RGW; ++i) {
+      if (S::NREG % kWaves == 0 || wave + i * kWaves < S::NREG) {  // wave-uniform
         const int byte = (wave + i * kWaves) * 1024 + lane * 16;
         const int pl = byte / S::ROWB;
         const int off = min((((byte % S::ROWB) / 16) ^ swz(pl)) * 8, D - 8);
@@ -208,8 +215,12 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // its visible pools) goes to `gmax`; the selection reads those first and then only
   // the groups that can hold a winner.  Pools at or past p_end are invisible to every
   // row of the tile, so store_lim (visible and below p_end) bounds both stores.
-  const bool row_ok = wr0 + lg < nrows;
-  const int store_lim = row_ok ? min(my_nvis, p_end) : 0;
+  int store_lim[kQuads];
+#pragma unroll
+  for (int j = 0; j < kQuads; ++j) {
+    const int rr = wr0 + 4 * j + lg;
+    store_lim[j] = rr < nrows ? min((int)((t0 + rr) / kpool) + 1, p_end) : 0;
+  }
   // A stage's reduced scores stay in registers (lane (g, c) holds pools 4c .. 4c + 3 of
   // row g) until its last sub-tile is reduced, then go out with one 16-byte store per
   // lane, so every score row is written in whole 256-byte runs.  A lane stores when its
@@ -220,24 +231,29 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // same 4 values plus 2 quad steps.  Both stores are issued by every wave, lanes with
   // nothing to store giving an offset at or past the buffer's range (the hardware range
   // check drops such stores; the ranges are at most 2 GiB), so a wave issues exactly 2
-  // stores per stage; the wait for the key DMA below relies on it.
+  // stores per row quad and stage; the wait for the key DMA below relies on it.
   constexpr uint32_t kDrop = 0x80000000u;
-  float vals[kSubs] = {};
-  auto flush = [&](int base, bool live) {
+  float vals[kQuads][kSubs] = {};
+  // lane-local part of the group max (the lane's 4 pools, over the row's visible pools)
+  auto flush_max = [&](int j, int base) {
     const int p0 = base + 4 * lc;
     float m = -__builtin_inff();
 #pragma unroll
-    for (int sub = 0; sub < kSubs; ++sub) m = fmaxf(m, p0 + sub < store_lim ? vals[sub] : -__builtin_inff());
+    for (int sub = 0; sub < kSubs; ++sub) m = fmaxf(m, p0 + sub < store_lim[j] ? vals[j][sub] : -__builtin_inff());
+    return m;
+  };
+  auto flush_store = [&](int j, int base, bool live, float m) {
+    const int p0 = base + 4 * lc;
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
-    const bool vis = live && p0 < store_lim;
+    const bool vis = live && p0 < store_lim[j];
 #if defined(__HIP_DEVICE_COMPILE__)
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 u = {__float_as_uint(vals[0]), __float_as_uint(vals[1]), __float_as_uint(vals[2]),
-                     __float_as_uint(vals[3])};
-    __builtin_amdgcn_raw_buffer_store_b128(u, rs_out, vis ? orow_off + 4u * (uint32_t)p0 : kDrop, 0, 0);
+    const u32x4 u = {__float_as_uint(vals[j][0]), __float_as_uint(vals[j][1]),
+                     __float_as_uint(vals[j][2]), __float_as_uint(vals[j][3])};
+    __builtin_amdgcn_raw_buffer_store_b128(u, rs_out, vis ? orow_off[j] + 4u * (uint32_t)p0 : kDrop, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs_gmax,
-                                          vis && (lc & 3) == 0 ? grow_off + 4u * (uint32_t)(p0 / kSub) : kDrop,
+                                          vis && (lc & 3) == 0 ? grow_off[j] + 4u * (uint32_t)(p0 / kSub) : kDrop,
                                           0, 0);
 #endif
   };
@@ -246,10 +262,9 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // K steps back to back (the accumulator dependence is forwarded inside the matrix
   // pipe), and while chain c runs, the VALU works on the epilogue (ReLU and head weights
   // of its 4 outputs) of the chain two places before it, whose MFMAs have completed by
-  // then; chains 0 and 1 take the previous sub-tile's last two chains, and chain 1 then
-  // that sub-tile's head-sum reduction and store.  The epilogue thus interleaves with
-  // the MFMAs at about two VALU instructions per MFMA, and only three chains'
-  // accumulators are live.  Every row accumulates its heads in the same order
+  // then (chains 0 and 1 take the previous sub-tile's last two).  The epilogue thus
+  // interleaves with the MFMAs at two VALU instructions per MFMA, and only three
+  // chains' accumulators are live.  Every row accumulates its heads in the same order
   // (block 0, then block 1; the lane's 4 heads in order), so a score does not depend on
   // which slot of a wave its row occupies.
   constexpr int NCH = kRowsPerWave * S::MB;
@@ -261,14 +276,15 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[r] = fmaf(fmaxf(pb[i], 0.0f), sw[r][mb][i], x[r]);
   };
-  // lane group g ends up holding row g: ((g0 + g1) + (g2 + g3)) for every row
-  auto reduce = [&]() {
-    const float y01 = swap16_sum(x[0], x[1]);
-    const float y23 = swap16_sum(x[2], x[3]);
+  // row quad j: lane group g ends up holding row 4j + g, ((g0 + g1) + (g2 + g3)) for
+  // every row
+  auto reduce = [&](int j) {
+    const float y01 = swap16_sum(x[4 * j], x[4 * j + 1]);
+    const float y23 = swap16_sum(x[4 * j + 2], x[4 * j + 3]);
     // permlane32_swap(y01, y23): [y01.lo, y23.lo] + [y01.hi, y23.hi]
     auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01), __float_as_uint(y23), false, false);
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) x[r] = 0.0f;
+    for (int r = 0; r < 4; ++r) x[4 * j + r] = 0.0f;
     return __uint_as_float(z[0]) + __uint_as_float(z[1]);
   };
   auto b_read = [&](const unsigned char *sb, int sub, int ks) {
@@ -279,65 +295,118 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   dma_stage(p_begin, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first stage's keys have landed
   __syncthreads();
+  // Explicit schedule.  Each chain is one scheduling region (a full scheduling barrier
+  // after it), in which its K-step MFMAs alternate with the VALU work assigned to it:
+  // the epilogue of the chain two places before it, and at fixed chain positions the
+  // reduction of a row quad or one half of its store, so no VALU work piles up between
+  // MFMAs.  Positions count chains from the start of a stage; quad j of sub-tile s is
+  // complete once the epilogue of its last chain has run, and is reduced one chain
+  // later, at red_pos(j, s), which for the last quad of the last sub-tile falls into
+  // the next stage (kStageChains and beyond).  The stores of a stage's quad follow its
+  // last reduction (first half: masked group max; second half: quad max and the two
+  // stores).
+  constexpr int kStageChains = kSubs * NCH;
+  auto red_pos = [](int j, int s) { return s * NCH + 4 * (j + 1) * S::MB + 2; };
+  auto fa_pos = [&](int j) { return red_pos(j, kSubs - 1) + 1; };
+  float mloc[kQuads];
+#pragma unroll
+  for (int j = 0; j < kQuads; ++j) mloc[j] = -__builtin_inff();
+  auto extras = [&](int pos, int stage_base, int st) {
+#pragma unroll
+    for (int j = 0; j < kQuads; ++j) {
+#pragma unroll
+      for (int s = 0; s < kSubs; ++s)
+        if (red_pos(j, s) == pos) vals[j][s] = reduce(j);
+      // wa / wb: the half runs in the stage after the one whose values it stores
+      const int wa = fa_pos(j) >= kStageChains, wb = fa_pos(j) + 1 >= kStageChains;
+      if (fa_pos(j) == pos) mloc[j] = flush_max(j, stage_base - wa * kStagePools);
+      if (fa_pos(j) + 1 == pos) flush_store(j, stage_base - wb * kStagePools, st >= wb, mloc[j]);
+    }
+  };
+  // a scheduling group of n VALU instructions (the builtin takes a constant)
+  auto valu_group = [](int n) {
+    if (n <= 2) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    else if (n == 3) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    else if (n == 4) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    else if (n == 5) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    else if (n == 6) __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    else if (n == 7) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    else __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+  };
+  auto extra_valu = [&](int pos) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kQuads; ++j) {
+#pragma unroll
+      for (int s = 0; s < kSubs; ++s) n += red_pos(j, s) == pos ? 8 : 0;
+      n += fa_pos(j) == pos ? 14 : 0;
+      n += fa_pos(j) + 1 == pos ? 6 : 0;
+    }
+    return n;
+  };
   for (int st = 0; st < nstage; ++st) {
     const int stage_base = p_begin + st * kStagePools;
-    if (st + 1 < nstage) dma_stage(stage_base + kStagePools, (st + 1) & 1);
     const unsigned char *sb = lds + (st & 1) * S::STAGE_BYTES;
-    // B fragments are read one sub-tile ahead, so LDS latency hides behind the MFMAs.
     bf16x8 bb[2][S::KS];
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) bb[0][ks] = b_read(sb, 0, ks);
-
-#pragma unroll
     for (int sub = 0; sub < kSubs; ++sub) {
-      if (sub + 1 < kSubs) {
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) bb[(sub + 1) & 1][ks] = b_read(sb, sub + 1, ks);
-      }
       const bf16x8 (&b)[S::KS] = bb[sub & 1];
-#if KPOOL_SCORE_SCHED
-      // the next sub-tile's B reads go out first, ahead of this sub-tile's MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-#endif
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
+        const int gp = sub * NCH + c;
+        if (gp == 0) {
+          // the next stage's key DMA goes out before any of this stage's stores
+          if (st + 1 < nstage) dma_stage(stage_base + kStagePools, (st + 1) & 1);
+#pragma unroll
+          for (int ks = 0; ks < S::KS; ++ks) bb[0][ks] = b_read(sb, 0, ks);
+        }
+        if (c == 0 && sub + 1 < kSubs) {
+          // B fragments are read one sub-tile ahead
+#pragma unroll
+          for (int ks = 0; ks < S::KS; ++ks) bb[(sub + 1) & 1][ks] = b_read(sb, sub + 1, ks);
+        }
+        // reductions and stores due here (previous stage's when pos wraps); they read
+        // the head sums before this chain's epilogue updates them
+        extras(gp, stage_base, st);
+        extras(gp + kStageChains, stage_base, st);
         const int r = c / S::MB, mb = c % S::MB;
         floatx4 t = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], t, 0, 0, 0);
         epi((c + NCH - 2) % NCH);
-        if (c == 1) {
-          // the previous sub-tile (stage st - 1's last one when sub == 0) is complete,
-          // and with it, when sub == 0, the previous stage (the segment's first
-          // sub-tile has none: its zero state is not stored)
-          vals[(sub + kSubs - 1) % kSubs] = reduce();
-          if (sub == 0) flush(stage_base - kStagePools, st > 0);
-        }
         pb = pa;
         pa = t;
-#if KPOOL_SCORE_SCHED
+        if (gp != 0) {  // (the stage's first chain, behind the DMA and LDS reads, is left free)
+          // the epilogue's 8 VALU and the extras' estimated count, spread over the K steps
+          const int nv = (8 + extra_valu(gp) + extra_valu(gp + kStageChains) + S::KS - 1) / S::KS;
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+          for (int ks = 0; ks < S::KS; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            valu_group(nv);
+          }
         }
-#endif
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // This wave's key DMA for the next stage must have landed before the barrier
     // releases the other waves to read it: the barrier's fence does not cover LDS DMA,
     // so wait on vmcnt explicitly.  Vector memory operations complete in issue order for
-    // this counter, and this stage issued 2 stores after the DMA (the previous stage's
-    // scores and group maxima), so vmcnt(2) covers the DMA without waiting for them.
-    __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2), no other counter
+    // this counter, and this stage issued 2 stores per row quad after the DMA, so
+    // vmcnt(2 * kQuads) covers the DMA without waiting for them.
+    static_assert(2 * kQuads < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kQuads));  // vmcnt(2 * kQuads), no other counter
     __syncthreads();
   }
-  // drain: the last two chains' epilogues, then the last sub-tile's reduction and store
+  // drain: the last two chains' epilogues, then the reductions and stores that fall
+  // past the last stage
   epi(NCH - 2);
   pb = pa;
   epi(NCH - 1);
-  vals[kSubs - 1] = reduce();
-  flush(p_begin + (nstage - 1) * kStagePools, true);
+  {
+    const int last_base = p_begin + (nstage - 1) * kStagePools;
+#pragma unroll
+    for (int pos = kStageChains; pos < 2 * kStageChains; ++pos) extras(pos, last_base + kStagePools, nstage);
+  }
 }
 
 template <int H, int D>
