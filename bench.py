@@ -19,6 +19,10 @@ synthetic seeded inputs already resident in HBM.  Prints ONE JSON line:
               spans include the other stream's kernels)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
               workload's rows, extrapolated to the whole job by visible pairs
+  probe_peaks what this machine reaches on plain work, measured after the kernel
+              pass: a 1 GiB device-to-device copy (HBM) and a large bf16 GEMM
+              through torch.matmul (the vendor BLAS), with the score and top-k
+              rates as fractions of them beside the nominal-peak fractions
 
 The pages' own figure for this workload (KPool selection at 512k tokens on
 one B200, 21.07 s) is reported as context only.
@@ -126,6 +130,46 @@ def cpu_baseline(wl, inp, total_pairs, seed, budget_s=15.0):
                    f"by visible pairs = {est_full_s:.0f} s; host {cpu_model or platform.processor()}, "
                    f"{cores} cores visible, BLAS threads {threads}"),
     }
+
+
+def probe_peaks(reps: int = 10):
+    """Achievable rates on this machine: HBM by a plain device copy, bf16 MFMA by a GEMM.
+
+    Both run after the timed region and the kernel pass, so they change nothing
+    the bench line times.  The copy moves 1 GiB (read) + 1 GiB (write) per rep;
+    the GEMM is [16384, 16384] x [16384, 16384] in bf16 with fp32 accumulation
+    (2 * 16384^3 flop per rep), both operands contiguous.
+    """
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * a.numel() * 4 * reps / (e0.elapsed_time(e1) / 1000.0) / 1e9
+    del a, b
+    n = 16384  # (of 4096, 8192, 12288, 16384 the fastest on this chip)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+    y = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+    z = torch.matmul(x, y)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(reps):
+        z = torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) / 1000.0) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": copy_gbs, "bf16_gemm_TFLOPs": gemm_tflops,
+            "how": (f"{reps} x 1 GiB device-to-device copy (2 GiB moved each); {reps} x "
+                    f"torch.matmul bf16 [{n},{n}] x [{n},{n}]; HIP events")}
 
 
 def score_traffic(workload: str):
@@ -307,6 +351,11 @@ def main():
                                           if wl.name in PAGES_B200_SELECTION_S else None),
         },
     }
+    pk = probe_peaks()
+    pk["score_frac_of_gemm"] = score_tflops / pk["bf16_gemm_TFLOPs"]
+    pk["topk_frac_of_copy"] = topk_gbs / pk["hbm_copy_GBs"]
+    result["probe_peaks"] = pk
+    log(f"[bench] probes: copy {pk['hbm_copy_GBs']:.0f} GB/s, bf16 GEMM {pk['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         result["cpu_baseline"] = cpu_baseline(wl, inp, pairs, args.seed, args.cpu_seconds)
