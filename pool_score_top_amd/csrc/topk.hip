@@ -107,7 +107,8 @@ __device__ inline void wave_sort_desc(uint32_t (&x)[NMAX], int lane) {
           const uint32_t p = __shfl_xor(x[i], j);
           const bool lower = (e & j) == 0;
           const bool desc = (e & k) == 0;
-          x[i] = (lower == desc) ? max(x[i], p) : min(x[i], p);
+          // keep the larger value when lower == desc: take p when that comparison says so
+          x[i] = ((p > x[i]) == (lower == desc)) ? p : x[i];
         }
       }
     }
@@ -139,7 +140,7 @@ __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const uint64_t p = buf[m * kThreads + (tid ^ d)];
-        v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
+        v[m] = ((p > v[m]) == (lower == desc)) ? p : v[m];  // larger kept when lower == desc
       }
     }
     // distances across lanes of one wave
@@ -151,7 +152,7 @@ __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const uint64_t p = shfl_xor_u64(v[m], d);
-        v[m] = (lower == desc) ? (v[m] > p ? v[m] : p) : (v[m] < p ? v[m] : p);
+        v[m] = ((p > v[m]) == (lower == desc)) ? p : v[m];  // larger kept when lower == desc
       }
     }
     // distances inside a thread
@@ -163,7 +164,7 @@ __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
           if ((m & j) == 0) {
             const bool desc = ((e0 + m) & k) == 0;
             const uint64_t a = v[m], b = v[m | j];
-            const bool sw = desc ? (a < b) : (a > b);
+            const bool sw = (a < b) == desc;  // (keys are unique; equal padding zeros need no swap)
             v[m] = sw ? b : a;
             v[m | j] = sw ? a : b;
           }
