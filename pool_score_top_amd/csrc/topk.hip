@@ -7,17 +7,18 @@
 //
 // Each element is ranked by the 64-bit key (order_key(score) << 32 | ~index):
 // a larger key is better, and keys are unique, so "the best `budget` keys" is
-// exactly the selection.  One 512-thread workgroup owns one row, and several
-// of them share a CU, so their memory latencies overlap:
+// exactly the selection.  One workgroup owns one row, and several of them share
+// a CU, so their memory latencies overlap.  Two instances: 256 threads with
+// NMAX = 4 maxima per thread for budgets up to 512, 512 threads with NMAX = 8 up
+// to 2048.
 //
 //   pass 1  (HBM)   every thread keeps NMAX maxima over disjoint parts of its
 //                   elements (or, for long rows, of its 16-pool group maxima,
-//                   written by the score kernel): NMAX = 2 for budgets up to
-//                   1024, 8 up to 2048.  In each wave the ceil(budget/8)-th
-//                   largest of its 64*NMAX maxima is found by a register bitonic
-//                   sort; the minimum L over the 8 waves is a lower bound on the
-//                   budget-th best key (at least budget distinct elements reach
-//                   it).
+//                   written by the score kernel).  In each wave the
+//                   ceil(budget/waves)-th largest of its 64*NMAX maxima is found
+//                   by a radix descent with ballots; the minimum L over the waves
+//                   is a lower bound on the budget-th best key (at least budget
+//                   distinct elements reach it).
 //   pass 2  (L2)    elements with key >= L (for long rows: only inside the
 //                   groups whose max reaches L) are appended to an LDS candidate
 //                   list with one atomic per wave per step.  For iid scores the
@@ -81,38 +82,25 @@ __device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// 64*NMAX values of a wave (element e = i*64 + lane in x[i]) sorted descending in
-// place: afterwards x[i] of lane l holds the (i*64 + l)-th largest.
+// The rank-th largest (1-based, duplicates counted) of the wave's 64*NMAX values,
+// by a radix descent over the 32 bits: at each bit, the values that match the bits
+// decided so far and have this bit set are counted with ballots; if there are at
+// least `rank` of them the answer has the bit set, otherwise it has the bit clear
+// and those values are skipped.  The result is wave-uniform.
 template <int NMAX>
-__device__ inline void wave_sort_desc(uint32_t (&x)[NMAX], int lane) {
+__device__ inline uint32_t wave_kth_desc(const uint32_t (&x)[NMAX], int rank) {
+  uint32_t prefix = 0;
+  int r = rank;
 #pragma unroll
-  for (int k = 2; k <= 64 * NMAX; k <<= 1) {
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t want = (prefix >> b) | 1u;  // decided bits above b, then bit b set
+    int cnt = 0;
 #pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 64) {  // the pair sits in one lane, registers i and i ^ (j / 64)
-        const int jr = j / 64;
-#pragma unroll
-        for (int i = 0; i < NMAX; ++i) {
-          if ((i & jr) == 0) {
-            const bool desc = ((i * 64) & k) == 0;  // k >= 128: lane bits play no part
-            const uint32_t a = x[i], b = x[i | jr];
-            x[i] = desc ? max(a, b) : min(a, b);
-            x[i | jr] = desc ? min(a, b) : max(a, b);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < NMAX; ++i) {
-          const int e = i * 64 + lane;
-          const uint32_t p = __shfl_xor(x[i], j);
-          const bool lower = (e & j) == 0;
-          const bool desc = (e & k) == 0;
-          // keep the larger value when lower == desc: take p when that comparison says so
-          x[i] = ((p > x[i]) == (lower == desc)) ? p : x[i];
-        }
-      }
-    }
+    for (int i = 0; i < NMAX; ++i) cnt += __popcll(__ballot((x[i] >> b) == want));
+    if (cnt >= r) prefix |= 1u << b;
+    else r -= cnt;
   }
+  return prefix;
 }
 
 // Bitonic sort (descending) of kThreads*M keys in a blocked layout: thread t holds
@@ -378,13 +366,8 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
         }
       }
     }
-    wave_sort_desc<NMAX>(tmax, lane);
     const int rank = (budget + kWavesT - 1) / kWavesT;  // 1..64*NMAX
-    uint32_t pick = tmax[0];
-#pragma unroll
-    for (int i = 1; i < NMAX; ++i)
-      if ((rank - 1) / 64 == i) pick = tmax[i];
-    const uint32_t wb = __shfl(pick, (rank - 1) & 63);
+    const uint32_t wb = wave_kth_desc<NMAX>(tmax, rank);
     if (lane == 0) sm.wave_bound[wave] = wb;
     __syncthreads();
     bound = sm.wave_bound[0];
