@@ -82,6 +82,13 @@ __device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The float whose order key is k, for k = 0 (a NaN) or a key of a non-NaN value
+// (k >= order_key(-inf)); with it, order_key(x) >= k reads as x >= key_float(k)
+// for every non-NaN x when k != 0, and NaN (key 0) never passes.
+__device__ inline float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // The rank-th largest (1-based, duplicates counted) of the wave's 64*NMAX values,
 // by a radix descent over the 32 bits: at each bit, the values that match the bits
 // decided so far and have this bit set are counted with ballots; if there are at
@@ -254,8 +261,9 @@ __device__ inline void next_digit(SM &sm, uint64_t prefix, int pbits, int krem, 
 }
 
 // Append the elements of one float4 piece at `base` whose key reaches `bound`.
+// (Positions are 32-bit: a row holds fewer than 2^31 elements.)
 template <int NMAX>
-__device__ inline void append_piece(const float4 x, int64_t base, int64_t n, uint32_t bound,
+__device__ inline void append_piece(const float4 x, int32_t base, int32_t n, uint32_t bound,
                                     Smem<NMAX> &sm, int lane) {
   constexpr int kCandCap = Cfg<NMAX>::kCand;
   const float xs[4] = {x.x, x.y, x.z, x.w};
@@ -328,9 +336,12 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
   // elements.
   uint32_t bound = 0;
   if (n > budget) {
-    uint32_t tmax[NMAX];
+    // The maxima are taken in the float domain (fmaxf skips NaN, and order_key is
+    // monotonic on the rest, -0 and +0 sharing a key), then turned into keys; a slot
+    // that saw only NaNs stays NaN, key 0.
+    float fmx[NMAX];
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) tmax[i] = 0;
+    for (int i = 0; i < NMAX; ++i) fmx[i] = __uint_as_float(0x7FC00000u);
     if (use_groups) {
       // rounds of kRound independent loads per thread; item j goes to maximum j % NMAX
       for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
@@ -338,15 +349,9 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
           v[j] = grow[min(gb + tid + (int64_t)j * kThreads, ng - 1)];
-        // A group max must not exceed the best key actually in its group.  The score
-        // kernel's max skips NaN (key 0), so a group of NaNs reports -inf: count it
-        // as key 0 here.  (Pass 2 keeps -inf, an upper bound for such a group.)
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
-          if (gb + tid + (int64_t)j * kThreads < ng) {
-            const uint32_t k = order_key(v[j]);
-            tmax[j % NMAX] = max(tmax[j % NMAX], k == kNegInfKey ? 0u : k);
-          }
+          if (gb + tid + (int64_t)j * kThreads < ng) fmx[j % NMAX] = fmaxf(fmx[j % NMAX], v[j]);
       }
     } else {
       // NMAX/4 float4 pieces per thread per step; element e of piece q goes to
@@ -361,10 +366,19 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
             const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (base + e < n) tmax[4 * q + e] = max(tmax[4 * q + e], order_key(xs[e]));
+              if (base + e < n) fmx[4 * q + e] = fmaxf(fmx[4 * q + e], xs[e]);
           }
         }
       }
+    }
+    uint32_t tmax[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+      tmax[i] = order_key(fmx[i]);
+      // A group max must not exceed the best key actually in its group.  The score
+      // kernel's max skips NaN (key 0), so a group of NaNs reports -inf: count it as
+      // key 0 here.  (Pass 2 keeps -inf, an upper bound for such a group.)
+      if (use_groups && tmax[i] == kNegInfKey) tmax[i] = 0;
     }
     const int rank = (budget + kWavesT - 1) / kWavesT;  // 1..64*NMAX
     const uint32_t wb = wave_kth_desc<NMAX>(tmax, rank);
@@ -375,6 +389,9 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     for (int w = 1; w < kWavesT; ++w) bound = min(bound, sm.wave_bound[w]);
   }
   __syncthreads();
+  // the bound as a float test for the group maxima (key 0 takes every group)
+  const bool take_all = bound == 0;
+  const float bf = key_float(bound);
 
   // ---- pass 2: gather candidates with key >= bound ------------------------
   if (use_groups) {
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
         const int64_t g = gb + tid + (int64_t)j * kThreads;
-        const bool sel = g < ng && order_key(v[j]) >= bound;
+        const bool sel = g < ng && (take_all || v[j] >= bf);
         selm |= sel ? (1u << j) : 0u;
         c += sel ? 1u : 0u;
       }
@@ -408,26 +425,28 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
       if (tid == 0) sm.count = kCandCap + 1;  // too many groups: exact fallback below
     } else {
       // four threads per group, one float4 each; rounds of kPieces loads per thread
-      const int64_t npieces = 4 * (int64_t)gcount;
-      for (int64_t pb = 0; pb < npieces; pb += (int64_t)kThreads * kPieces) {
+      const int32_t n32 = (int32_t)n;
+      const int32_t npieces = 4 * (int32_t)gcount;
+      for (int32_t pb = 0; pb < npieces; pb += kThreads * kPieces) {
         float4 x[kPieces];
-        int64_t base[kPieces];
+        int32_t base[kPieces];
 #pragma unroll
         for (int j = 0; j < kPieces; ++j) {
-          const int64_t i = pb + tid + (int64_t)j * kThreads;
-          base[j] = i < npieces ? (int64_t)sm.glist[i >> 2] * kGroup + (i & 3) * 4 : n;
-          x[j] = *reinterpret_cast<const float4 *>(row + (base[j] < n ? base[j] : 0));
+          const int32_t i = pb + tid + j * kThreads;
+          base[j] = i < npieces ? (int32_t)sm.glist[i >> 2] * kGroup + (i & 3) * 4 : n32;
+          x[j] = *reinterpret_cast<const float4 *>(row + (base[j] < n32 ? base[j] : 0));
         }
 #pragma unroll
-        for (int j = 0; j < kPieces; ++j) append_piece(x[j], base[j], n, bound, sm, lane);
+        for (int j = 0; j < kPieces; ++j) append_piece(x[j], base[j], n32, bound, sm, lane);
       }
     }
   } else {
-    for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
-      const int64_t base = wbase + 4 * lane;
-      const float4 x = base < n ? *reinterpret_cast<const float4 *>(row + base)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-      append_piece(x, base, n, bound, sm, lane);
+    const int32_t n32 = (int32_t)n;
+    for (int32_t wbase = wave * 256; wbase < n32; wbase += kThreads * 4) {
+      const int32_t base = wbase + 4 * lane;
+      const float4 x = base < n32 ? *reinterpret_cast<const float4 *>(row + base)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      append_piece(x, base, n32, bound, sm, lane);
     }
   }
   __syncthreads();
