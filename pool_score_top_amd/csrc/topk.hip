@@ -75,6 +75,14 @@ struct Cfg {
 __device__ inline uint64_t compose(uint32_t okey, uint32_t idx) {
   return ((uint64_t)okey << 32) | (uint64_t)(~idx);
 }
+// Candidates are appended as (float bits << 32 | ~index) and turned into keys once
+// the list is complete, where it is dense.
+__device__ inline uint64_t compose_raw(float x, uint32_t idx) {
+  return ((uint64_t)__float_as_uint(x) << 32) | (uint64_t)(~idx);
+}
+__device__ inline uint64_t raw_to_key(uint64_t r) {
+  return ((uint64_t)order_key(__uint_as_float((uint32_t)(r >> 32))) << 32) | (r & 0xFFFFFFFFull);
+}
 
 __device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
   const uint32_t lo = __shfl_xor((unsigned)(uint32_t)v, mask);
@@ -260,28 +268,38 @@ __device__ inline void next_digit(SM &sm, uint64_t prefix, int pbits, int krem, 
   }
 }
 
-// Append the elements of one float4 piece at `base` whose key reaches `bound`.
-// (Positions are 32-bit: a row holds fewer than 2^31 elements.)
+// Append the elements of one float4 piece at `base` whose key reaches the bound
+// (take_all: the bound is key 0, which every element reaches; otherwise the test is
+// x >= bf in floats, see key_float), in raw form.  (Positions are 32-bit: a row
+// holds fewer than 2^31 elements.)
 template <int NMAX>
-__device__ inline void append_piece(const float4 x, int32_t base, int32_t n, uint32_t bound,
+__device__ inline void append_piece(const float4 x, int32_t base, int32_t n, bool take_all, float bf,
                                     Smem<NMAX> &sm, int lane) {
   constexpr int kCandCap = Cfg<NMAX>::kCand;
   const float xs[4] = {x.x, x.y, x.z, x.w};
-  uint32_t keys[4];
+  // One ballot per element slot: the wave's selected elements of slot e go to
+  // consecutive positions after those of slots 0 .. e-1 (the list's order is free).
   bool sel[4];
-  uint32_t c = 0;
+  uint64_t msk[4];
+  uint32_t off[4], tot = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    keys[e] = order_key(xs[e]);
-    sel[e] = (base + e < n) && keys[e] >= bound;
-    c += sel[e] ? 1u : 0u;
+    // (bitwise, so that each test stays a lane mask)
+    sel[e] = (base + e < n) & (take_all | (xs[e] >= bf));
+    msk[e] = __ballot(sel[e]);
+    off[e] = tot;
+    tot += (uint32_t)__popcll(msk[e]);
   }
-  uint32_t pos = wave_reserve<3>(c, &sm.count, lane);
+  if (tot == 0) return;  // wave-uniform
+  uint32_t wbase = 0;
+  if (lane == 0) wbase = atomicAdd(&sm.count, tot);
+  wbase = __builtin_amdgcn_readfirstlane(wbase);  // every lane is active here
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (sel[e]) {
-      if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose(keys[e], (uint32_t)(base + e));
-      ++pos;
+      const uint32_t pos = wbase + off[e] +
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(msk[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk[e], 0u));
+      if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose_raw(xs[e], (uint32_t)(base + e));
     }
   }
 }
@@ -389,33 +407,41 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     for (int w = 1; w < kWavesT; ++w) bound = min(bound, sm.wave_bound[w]);
   }
   __syncthreads();
-  // the bound as a float test for the group maxima (key 0 takes every group)
+  // the bound as a float test (key 0 takes every element, NaN included)
   const bool take_all = bound == 0;
   const float bf = key_float(bound);
 
   // ---- pass 2: gather candidates with key >= bound ------------------------
   if (use_groups) {
-    // groups whose max reaches the bound (uniform trip count; loads issued per round)
-    for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
+    // groups whose max reaches the bound (uniform trip count; loads issued per round).
+    // One ballot per load slot j: the wave's selected groups of slot j go to
+    // consecutive positions after those of slots 0 .. j-1.  (Group indices are
+    // 32-bit: a row has fewer than 2^27 groups.)
+    const int32_t ng32 = (int32_t)ng;
+    for (int32_t gb = 0; gb < ng32; gb += kThreads * kRound) {
       float v[kRound];
 #pragma unroll
-      for (int j = 0; j < kRound; ++j)
-        v[j] = grow[min(gb + tid + (int64_t)j * kThreads, ng - 1)];
-      uint32_t selm = 0, c = 0;
+      for (int j = 0; j < kRound; ++j) v[j] = grow[min(gb + tid + j * kThreads, ng32 - 1)];
+      bool sel[kRound];
+      uint64_t msk[kRound];
+      uint32_t off[kRound], tot = 0;
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
-        const int64_t g = gb + tid + (int64_t)j * kThreads;
-        const bool sel = g < ng && (take_all || v[j] >= bf);
-        selm |= sel ? (1u << j) : 0u;
-        c += sel ? 1u : 0u;
+        sel[j] = (gb + tid + j * kThreads < ng32) & (take_all | (v[j] >= bf));
+        msk[j] = __ballot(sel[j]);
+        off[j] = tot;
+        tot += (uint32_t)__popcll(msk[j]);
       }
-      static_assert(kRound < 16, "per-thread count fits 4 bits");
-      uint32_t pos = wave_reserve<4>(c, &sm.gcount, lane);
+      if (tot == 0) continue;  // wave-uniform
+      uint32_t wbase = 0;
+      if (lane == 0) wbase = atomicAdd(&sm.gcount, tot);
+      wbase = __builtin_amdgcn_readfirstlane(wbase);  // every lane is active here
 #pragma unroll
       for (int j = 0; j < kRound; ++j) {
-        if (selm & (1u << j)) {
-          if (pos < (uint32_t)kGroupCap) sm.glist[pos] = (uint32_t)(gb + tid + (int64_t)j * kThreads);
-          ++pos;
+        if (sel[j]) {
+          const uint32_t pos = wbase + off[j] +
+              __builtin_amdgcn_mbcnt_hi((uint32_t)(msk[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk[j], 0u));
+          if (pos < (uint32_t)kGroupCap) sm.glist[pos] = (uint32_t)(gb + tid + j * kThreads);
         }
       }
     }
@@ -437,7 +463,7 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
           x[j] = *reinterpret_cast<const float4 *>(row + (base[j] < n32 ? base[j] : 0));
         }
 #pragma unroll
-        for (int j = 0; j < kPieces; ++j) append_piece(x[j], base[j], n32, bound, sm, lane);
+        for (int j = 0; j < kPieces; ++j) append_piece(x[j], base[j], n32, take_all, bf, sm, lane);
       }
     }
   } else {
@@ -446,7 +472,7 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
       const int32_t base = wbase + 4 * lane;
       const float4 x = base < n32 ? *reinterpret_cast<const float4 *>(row + base)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-      append_piece(x, base, n32, bound, sm, lane);
+      append_piece(x, base, n32, take_all, bf, sm, lane);
     }
   }
   __syncthreads();
@@ -486,11 +512,15 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     for (int64_t wbase = (int64_t)wave * 256; wbase < n; wbase += kThreads * 4) {
       const int64_t base = wbase + 4 * lane;
       uint64_t cks[4] = {0, 0, 0, 0};
+      float xs[4] = {0.f, 0.f, 0.f, 0.f};
       bool sel[4] = {false, false, false, false};
       uint32_t c = 0;
       if (base < n) {
         const float4 x = *reinterpret_cast<const float4 *>(row + base);
-        const float xs[4] = {x.x, x.y, x.z, x.w};
+        xs[0] = x.x;
+        xs[1] = x.y;
+        xs[2] = x.z;
+        xs[3] = x.w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           cks[e] = compose(order_key(xs[e]), (uint32_t)(base + e));
@@ -502,7 +532,7 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (sel[e]) {
-          if (pos < (uint32_t)kCandCap) sm.cand[pos] = cks[e];
+          if (pos < (uint32_t)kCandCap) sm.cand[pos] = compose_raw(xs[e], (uint32_t)(base + e));
           ++pos;
         }
       }
@@ -510,6 +540,9 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     __syncthreads();
     count = min(sm.count, (uint32_t)kCandCap);
   }
+  // raw entries -> keys
+  for (uint32_t i = tid; i < count; i += kThreads) sm.cand[i] = raw_to_key(sm.cand[i]);
+  __syncthreads();
 
   // ---- exact cut to `budget` keys when that shrinks the sort ----------------
   // A radix select over the LDS list (8-bit digits of the unique 64-bit keys, usually
