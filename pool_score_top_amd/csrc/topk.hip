@@ -53,7 +53,8 @@ constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // order_key(-inf)
 // groups, at most 930 and 880 over 200 rows).  The top-k is latency-bound, so the
 // small instance is sized for rows in flight: lists of 1280 candidates and 1280
 // groups (16.4 KB of LDS) and rounds of 8 group maxima or 4 score pieces per thread
-// (52 VGPRs) let nine rows share a CU.  The large instance holds 4096 of each.  A row
+// (52 VGPRs) let eight rows share a CU, the limit of eight waves per SIMD.  The large
+// instance holds 4096 of each.  A row
 // that overflows a list takes the exact path, so the caps bound speed, not results.
 template <int NMAX>
 struct Cfg {
