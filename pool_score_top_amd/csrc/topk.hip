@@ -201,6 +201,7 @@ struct Smem {
   uint32_t glist[Cfg<NMAX>::kGroups];
   uint32_t hist[256];
   uint32_t wave_bound[Cfg<NMAX>::kWaves];
+  uint32_t wave_max[Cfg<NMAX>::kWaves];
   uint64_t prefix;
   uint32_t count;
   uint32_t gcount;
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
   // NMAX maxima per thread over disjoint parts of the row (its elements, or its
   // groups' maxima, which are elements too), so any budget of them are distinct
   // elements.
-  uint32_t bound = 0;
+  uint32_t bound = 0, rowmax = 0xFFFFFFFFu;
   if (n > budget) {
     // The maxima are taken in the float domain (fmaxf skips NaN, and order_key is
     // monotonic on the rest, -0 and +0 sharing a key), then turned into keys; a slot
@@ -391,21 +392,33 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
       }
     }
     uint32_t tmax[NMAX];
+    uint32_t lm = 0;  // the row's best key: every element is at most one of these maxima
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) {
       tmax[i] = order_key(fmx[i]);
+      lm = max(lm, tmax[i]);
       // A group max must not exceed the best key actually in its group.  The score
       // kernel's max skips NaN (key 0), so a group of NaNs reports -inf: count it as
-      // key 0 here.  (Pass 2 keeps -inf, an upper bound for such a group.)
+      // key 0 here.  (Pass 2 and the row's best key keep -inf, an upper bound for such
+      // a group.)
       if (use_groups && tmax[i] == kNegInfKey) tmax[i] = 0;
     }
     const int rank = (budget + kWavesT - 1) / kWavesT;  // 1..64*NMAX
     const uint32_t wb = wave_kth_desc<NMAX>(tmax, rank);
-    if (lane == 0) sm.wave_bound[wave] = wb;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lm = max(lm, (uint32_t)__shfl_xor((int)lm, o));
+    if (lane == 0) {
+      sm.wave_bound[wave] = wb;
+      sm.wave_max[wave] = lm;
+    }
     __syncthreads();
     bound = sm.wave_bound[0];
+    rowmax = sm.wave_max[0];
 #pragma unroll
-    for (int w = 1; w < kWavesT; ++w) bound = min(bound, sm.wave_bound[w]);
+    for (int w = 1; w < kWavesT; ++w) {
+      bound = min(bound, sm.wave_bound[w]);
+      rowmax = max(rowmax, sm.wave_max[w]);
+    }
   }
   __syncthreads();
   // the bound as a float test (key 0 takes every element, NaN included)
@@ -552,8 +565,13 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
   auto sort_class = [](uint32_t x) { return x <= kThreads ? 1 : x <= 2 * kThreads ? 2 : x <= 4 * kThreads ? 4 : 8; };
   uint64_t *list = sm.cand;
   if (count > (uint32_t)budget && sort_class(count) > sort_class((uint32_t)budget)) {
-    uint64_t prefix = 0;
-    int pbits = 0;
+    // Every candidate's top 32 key bits lie in [bound, rowmax], so all of them share
+    // the leading bits common to those two: the digits inside that prefix are skipped
+    // (for rows of similar scores the first one or two, whose histograms would put
+    // every key into one bin).
+    const int common = bound == rowmax ? 32 : __builtin_clz(bound ^ rowmax);
+    int pbits = common / 8 * 8;
+    uint64_t prefix = pbits ? ((uint64_t)rowmax >> (32 - pbits)) : 0ull;
     int krem = budget;
     for (int pass = 0; pass < 8; ++pass) {
       if (tid < 256) sm.hist[tid] = 0;
