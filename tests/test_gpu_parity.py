@@ -284,6 +284,12 @@ def _topk_rows(rng):
     z = rng.standard_normal(50000).astype(np.float32)
     z[1000:6000] = z.max() + 1.0                                                      # 5000 tied on top
     rows.append(z)
+    for t in (700, 2500):                  # ties on top between the budget and the list cap:
+        u = rng.standard_normal(65536).astype(np.float32)  # the cut starts past 32 shared bits
+        u[rng.choice(65536, t, replace=False)] = u.max() + 1.0
+        rows.append(u)
+    v = (1.0 + rng.integers(0, 4096, 65536) * 2.0 ** -20).astype(np.float32)
+    rows.append(v)                         # narrow range: bound and best key share ~20 bits
     ramp = np.arange(30000, dtype=np.float32)                                         # sorted input
     rows.append(ramp)
     rows.append(ramp[::-1].copy())
