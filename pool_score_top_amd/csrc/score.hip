@@ -347,10 +347,12 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   for (int st = 0; st < nstage; ++st) {
     const int stage_base = p_begin + st * kStagePools;
     const unsigned char *sb = lds + (st & 1) * S::STAGE_BYTES;
-    bf16x8 bb[2][S::KS];
+    // One set of B fragments: the next sub-tile's are read into the same registers
+    // right after the last chain's MFMAs of this one (a second set, read a whole
+    // sub-tile ahead, measured 0.5% slower and costs 14 VGPRs).
+    bf16x8 b[S::KS];
 #pragma unroll
     for (int sub = 0; sub < kSubs; ++sub) {
-      const bf16x8 (&b)[S::KS] = bb[sub & 1];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int gp = sub * NCH + c;
@@ -358,12 +360,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
           // the next stage's key DMA goes out before any of this stage's stores
           if (st + 1 < nstage) dma_stage(stage_base + kStagePools, (st + 1) & 1);
 #pragma unroll
-          for (int ks = 0; ks < S::KS; ++ks) bb[0][ks] = b_read(sb, 0, ks);
-        }
-        if (c == 0 && sub + 1 < kSubs) {
-          // B fragments are read one sub-tile ahead
-#pragma unroll
-          for (int ks = 0; ks < S::KS; ++ks) bb[(sub + 1) & 1][ks] = b_read(sb, sub + 1, ks);
+          for (int ks = 0; ks < S::KS; ++ks) b[ks] = b_read(sb, 0, ks);
         }
         // reductions and stores due here (previous stage's when pos wraps); they read
         // the head sums before this chain's epilogue updates them
@@ -373,6 +370,10 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
         floatx4 t = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r][mb][ks], b[ks], t, 0, 0, 0);
+        if (c == NCH - 1 && sub + 1 < kSubs) {
+#pragma unroll
+          for (int ks = 0; ks < S::KS; ++ks) b[ks] = b_read(sb, sub + 1, ks);
+        }
         epi((c + NCH - 2) % NCH);
         pb = pa;
         pa = t;
