@@ -253,14 +253,20 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i} done")
 
-    # timed region: K whole steps, nothing else on the GPU
+    # timed region: K whole steps, nothing else on the GPU.  Events on the stream the
+    # steps run on (the library joins its helper stream back into it) split the region
+    # into steps without a synchronization inside it.
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    step_ev[0].record()
     for i in range(args.steps):
         sel.run(inp["q"], inp["k"], inp["w"])
+        step_ev[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1000.0 * elapsed / args.steps
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
     log(f"[bench] {args.steps} steps, {ms_step:.2f} ms/step (overlap {args.overlap})")
 
     # kernel pass: the same steps with every launch alone on one stream, each bracketed
@@ -336,6 +342,8 @@ def main():
             "measured": ("HIP events around each launch on its stream, kernel pass of the same "
                          "steps with chunk overlap off"),
         },
+        "step_ms": {"median": float(np.median(step_ms)), "min": float(min(step_ms)),
+                    "max": float(max(step_ms)), "how": "HIP events between the timed steps"},
         "kernel_pass_ms_per_step": ms_serial,
         "kernels": {
             "score": {"ms_per_step": score_ms / S, "tflops": score_tflops,
