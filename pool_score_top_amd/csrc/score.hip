@@ -251,7 +251,12 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 u = {__float_as_uint(vals[j][0]), __float_as_uint(vals[j][1]),
                      __float_as_uint(vals[j][2]), __float_as_uint(vals[j][3])};
-    __builtin_amdgcn_raw_buffer_store_b128(u, rs_out, vis ? orow_off[j] + 4u * (uint32_t)p0 : kDrop, 0, 0);
+    // Scores are stored non-temporally (cache policy NT): they are written once and most of
+    // them are never read back, so they should not push the group maxima, which the
+    // selection reads next, out of the caches.
+    constexpr int kNonTemporal = 2;
+    __builtin_amdgcn_raw_buffer_store_b128(u, rs_out, vis ? orow_off[j] + 4u * (uint32_t)p0 : kDrop, 0,
+                                           kNonTemporal);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs_gmax,
                                           vis && (lc & 3) == 0 ? grow_off[j] + 4u * (uint32_t)(p0 / kSub) : kDrop,
                                           0, 0);
