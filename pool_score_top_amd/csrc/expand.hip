@@ -29,6 +29,9 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(const int32_t *_
     const int64_t t = i - cu_seqlens[s];
     const int32_t *prow = pool_ids + r * budget;
     int32_t *orow = tok + r * budget * kpool;
+    // The 16-byte token-id stores are non-temporal: the output is written once and not
+    // read again on the path.
+    typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
     if (kpool == 4) {
       for (int j = threadIdx.x; j < budget; j += kExpandThreads) {
         const int32_t p = prow[j];
@@ -38,13 +41,15 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(const int32_t *_
           const int64_t tk = (int64_t)p * 4 + k;
           v[k] = (p >= 0 && tk <= t) ? (int32_t)tk : -1;
         }
-        *reinterpret_cast<int4 *>(orow + 4 * j) = make_int4(v[0], v[1], v[2], v[3]);
+        const i32x4 o = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<i32x4 *>(orow + 4 * j));
       }
     } else if (kpool == 1 && vec) {
       for (int j = threadIdx.x; j < budget / 4; j += kExpandThreads) {
         const int4 p = reinterpret_cast<const int4 *>(prow)[j];
         auto f = [&](int32_t q) { return (q >= 0 && q <= t) ? q : -1; };
-        reinterpret_cast<int4 *>(orow)[j] = make_int4(f(p.x), f(p.y), f(p.z), f(p.w));
+        const i32x4 o = {f(p.x), f(p.y), f(p.z), f(p.w)};
+        __builtin_nontemporal_store(o, reinterpret_cast<i32x4 *>(orow) + j);
       }
     } else {
       const int64_t n = (int64_t)budget * kpool;

@@ -464,7 +464,10 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     if (gcount > (uint32_t)kGroupCap) {
       if (tid == 0) sm.count = kCandCap + 1;  // too many groups: exact fallback below
     } else {
-      // four threads per group, one float4 each; rounds of kPieces loads per thread
+      // four threads per group, one float4 each; rounds of kPieces loads per thread.  The
+      // loads are non-temporal: each score piece is read once, and the group maxima of
+      // the rows still to come should stay cached.
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
       const int32_t n32 = (int32_t)n;
       const int32_t npieces = 4 * (int32_t)gcount;
       for (int32_t pb = 0; pb < npieces; pb += kThreads * kPieces) {
@@ -474,7 +477,8 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
         for (int j = 0; j < kPieces; ++j) {
           const int32_t i = pb + tid + j * kThreads;
           base[j] = i < npieces ? (int32_t)sm.glist[i >> 2] * kGroup + (i & 3) * 4 : n32;
-          x[j] = *reinterpret_cast<const float4 *>(row + (base[j] < n32 ? base[j] : 0));
+          const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + (base[j] < n32 ? base[j] : 0)));
+          x[j] = make_float4(t.x, t.y, t.z, t.w);
         }
 #pragma unroll
         for (int j = 0; j < kPieces; ++j) append_piece(x[j], base[j], n32, take_all, bf, sm, lane);
