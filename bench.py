@@ -209,6 +209,9 @@ def main():
                     help="chunk overlap (two buffers on two streams) in the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--workspace-mib", type=int, default=None,
+                    help="cap the score workspace (default: two full 2 GiB chunk buffers); "
+                         "smaller workspaces mean shorter chunks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -243,7 +246,8 @@ def main():
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
     cu = inp["cu_seqlens"]
     q_lo, q_hi = wl.rows
-    sel = K.Selector(cu, wl.kpool, wl.budget, wl.H, wl.D, device=dev, q_lo=q_lo, q_hi=q_hi)
+    sel = K.Selector(cu, wl.kpool, wl.budget, wl.H, wl.D, device=dev, q_lo=q_lo, q_hi=q_hi,
+                     workspace_cap=None if args.workspace_mib is None else args.workspace_mib << 20)
     pairs = visible_pairs(cu, q_lo, q_hi, wl.kpool)
     flops = 2.0 * wl.H * wl.D * pairs
 
