@@ -435,7 +435,8 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     for (int32_t gb = 0; gb < ng32; gb += kThreads * kRound) {
       float v[kRound];
 #pragma unroll
-      for (int j = 0; j < kRound; ++j) v[j] = grow[min(gb + tid + j * kThreads, ng32 - 1)];
+      // (the row's last read of its group maxima: non-temporal)
+      for (int j = 0; j < kRound; ++j) v[j] = __builtin_nontemporal_load(grow + min(gb + tid + j * kThreads, ng32 - 1));
       bool sel[kRound];
       uint64_t msk[kRound];
       uint32_t off[kRound], tot = 0;
