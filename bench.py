@@ -172,30 +172,38 @@ def probe_peaks(reps: int = 10):
                     f"torch.matmul bf16 [{n},{n}] x [{n},{n}]; HIP events")}
 
 
-def score_traffic(workload: str):
-    """HBM bytes per score-kernel launch from the committed counter summary, or None.
+COUNTER_SOURCES = ("score.hip", "topk.hip", "api.hip")
 
-    The summary (profiles/score_kernel_sq524288_traffic.md) holds FETCH_SIZE and
-    WRITE_SIZE per launch, scaled by a plain-copy calibration, and the sha256 of
-    score.hip and of api.hip (which sizes the launches) it was measured on; a
-    changed kernel or launch plan makes the figure stale (None).
+
+def committed_counters(workload: str):
+    """Per-launch counter figures from the committed summary profiles/counters_<workload>.md.
+
+    The summary holds, per kernel, the FETCH_SIZE / WRITE_SIZE bytes per launch
+    (scaled by a plain-copy calibration) and the score kernel's MFMA-busy share,
+    from rocprofv3 --pmc runs of this script, together with the sha256 of the
+    sources they were measured on (score.hip, topk.hip and api.hip, which plans
+    the launches; the score kernel's cache policy also decides what the top-k
+    finds in the caches).  Any changed source makes the figures stale: None.
     """
     import hashlib
-    prof = os.path.join(ROOT, "profiles", f"score_kernel_{workload}_traffic.md")
+    prof = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
     csrc = os.path.join(ROOT, "pool_score_top_amd", "csrc")
     if not os.path.exists(prof):
         return None
     vals = {}
     for line in open(prof):
-        if ":" in line and line.strip().startswith("score_"):
+        line = line.strip()
+        if ":" in line and line.split(":", 1)[0].startswith(("sha256_", "score_", "topk_")):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    for key, name in (("score_hip_sha256", "score.hip"), ("score_api_hip_sha256", "api.hip")):
+    for name in COUNTER_SOURCES:
         sha = hashlib.sha256(open(os.path.join(csrc, name), "rb").read()).hexdigest()
-        if vals.get(key) != sha:
+        if vals.get(f"sha256_{name}") != sha:
             return None
-    return {"fetch": float(vals["score_fetch_bytes_per_launch"]),
-            "write": float(vals["score_write_bytes_per_launch"])}
+    try:
+        return {k: float(v) for k, v in vals.items() if not k.startswith("sha256_")}
+    except ValueError:
+        return None
 
 
 def main():
@@ -246,12 +254,13 @@ def main():
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
     cu = inp["cu_seqlens"]
     q_lo, q_hi = wl.rows
+    overlap = args.overlap == "on"
     sel = K.Selector(cu, wl.kpool, wl.budget, wl.H, wl.D, device=dev, q_lo=q_lo, q_hi=q_hi,
-                     workspace_cap=None if args.workspace_mib is None else args.workspace_mib << 20)
+                     workspace_cap=None if args.workspace_mib is None else args.workspace_mib << 20,
+                     overlap=overlap)
     pairs = visible_pairs(cu, q_lo, q_hi, wl.kpool)
     flops = 2.0 * wl.H * wl.D * pairs
 
-    K.set_overlap(args.overlap == "on")
     for i in range(args.warmup):
         sel.run(inp["q"], inp["k"], inp["w"])
         torch.cuda.synchronize()
@@ -273,20 +282,18 @@ def main():
     step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
     log(f"[bench] {args.steps} steps, {ms_step:.2f} ms/step (overlap {args.overlap})")
 
-    # kernel pass: the same steps with every launch alone on one stream, each bracketed
-    # by HIP events on that stream
-    K.set_overlap(False)
+    # kernel pass: the same steps with every launch alone on one stream (flags = 0; the
+    # same workspace gives the same chunks), each bracketed by HIP events on that stream
     K.profile_enable(True)
     K.profile_collect()  # reset
     torch.cuda.synchronize()
     tk = time.perf_counter()
     for i in range(args.steps):
-        sel.run(inp["q"], inp["k"], inp["w"])
+        sel.run(inp["q"], inp["k"], inp["w"], overlap=False)
     torch.cuda.synchronize()
     ms_serial = 1000.0 * (time.perf_counter() - tk) / args.steps
     prof = K.profile_collect()
     K.profile_enable(False)
-    K.set_overlap(True)
     log(f"[bench] kernel pass: {args.steps} steps, {ms_serial:.2f} ms/step (overlap off, events on)")
 
     score_ms, score_n = prof["score"]
@@ -303,11 +310,36 @@ def main():
     pool_bytes = 2.0 * wl.T * wl.D + 2.0 * sel.P_tot * wl.D
     pool_gbs = pool_bytes * S / (pool_ms / 1000.0) / 1e9 if pool_ms > 0 else 0.0
 
-    traffic = score_traffic(wl.name)
+    cnt = committed_counters(wl.name)
+    chunk_rows = sel.chunk_rows()
     pitch = ((sel.max_pools + 63) // 64) * 64
-    cap_rows = (1 << 31) // (pitch * 4)
-    buf_rows = sel.workspace.numel() // ((pitch + pitch // 16) * 4)
-    chunk_rows = int(min(cap_rows, buf_rows // 2 if (args.overlap == "on" and buf_rows >= 2) else buf_rows))
+    nbuf = 2 if overlap and sel.workspace_bytes >= 2 * (pitch + pitch // 16) * 4 else 1
+    score_launch_ms = score_ms / max(1, score_n)
+    topk_launch_ms = topk_ms / max(1, topk_n)
+    topk = {"ms_per_step": topk_ms / S, "launches_per_step": topk_n // S,
+            "avg_launch_ms": topk_launch_ms,
+            # 4 B per visible pair plus the ids, over the top-k time: the rate of a full
+            # scan.  The group-pruned kernel skips most of those bytes, so this is not an
+            # HBM rate and may exceed the peak.
+            "gbs_if_every_score_were_read": topk_gbs,
+            "frac_if_every_score_were_read": topk_gbs / PEAK_HBM_GBS}
+    if cnt is not None and "topk_fetch_bytes_per_launch" in cnt:
+        tb = cnt["topk_fetch_bytes_per_launch"] + cnt["topk_write_bytes_per_launch"]
+        topk.update({"traffic_bytes": tb,
+                     "traffic_read": cnt["topk_fetch_bytes_per_launch"],
+                     "traffic_write": cnt["topk_write_bytes_per_launch"],
+                     "achieved_GBs": tb / (topk_launch_ms / 1000.0) / 1e9,
+                     "peak_GBs": PEAK_HBM_GBS,
+                     "frac": tb / (topk_launch_ms / 1000.0) / 1e9 / PEAK_HBM_GBS,
+                     "how": ("HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE in the "
+                             f"committed profiles/counters_{wl.name}.md (copy-calibrated, sources "
+                             "hash-checked), over this run's average top-k launch time")})
+    else:
+        topk.update({"traffic_bytes": None, "achieved_GBs": None, "frac": None,
+                     "how": f"no current counter summary for {wl.name} (profiles/counters_{wl.name}.md)"})
+    score_traffic = None
+    if cnt is not None and "score_fetch_bytes_per_launch" in cnt:
+        score_traffic = (cnt["score_fetch_bytes_per_launch"], cnt["score_write_bytes_per_launch"])
     result = {
         "metric": "query-pool scores/s + selection wall time at 512k tokens, % MFMA/HBM peak",
         "value": pairs / (ms_step / 1000.0),
@@ -328,6 +360,10 @@ def main():
             "budget": wl.budget, "visible_pairs": pairs, "seed": args.seed,
             "score_chunk_rows": chunk_rows,
             "chunk_overlap": args.overlap,
+            "workspace_bytes": sel.workspace_bytes,
+            "chunk_buffers": nbuf,
+            "score_bytes_per_chunk_buffer": chunk_rows * pitch * 4,
+            "score_bytes_in_flight": nbuf * chunk_rows * pitch * 4,
         },
         "roofline": {
             "bound": "mfma",
@@ -336,15 +372,21 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": score_tflops / PEAK_BF16_TFLOPS,
-            "traffic": (None if traffic is None else traffic["fetch"] + traffic["write"]),
-            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "traffic_read": None if traffic is None else traffic["fetch"],
-            "traffic_write": None if traffic is None else traffic["write"],
+            "traffic": None if score_traffic is None else sum(score_traffic),
+            "traffic_unit": ("HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), taken "
+                             f"from the committed profiles/counters_{wl.name}.md, not measured in this "
+                             "run; null when the sources changed since"),
+            "traffic_read": None if score_traffic is None else score_traffic[0],
+            "traffic_write": None if score_traffic is None else score_traffic[1],
+            "mfma_busy_frac": None if cnt is None else cnt.get("score_mfma_busy_frac"),
+            "mfma_busy_how": ("SQ_VALU_MFMA_BUSY_CYCLES over the SIMD-cycles the chip was active "
+                              "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) during the score launches, from "
+                              "the same committed counter summary"),
             "launches_per_step": score_n // S,
             "flops_per_launch": flops / max(1, score_n // S),
-            "avg_launch_ms": score_ms / max(1, score_n),
+            "avg_launch_ms": score_launch_ms,
             "measured": ("HIP events around each launch on its stream, kernel pass of the same "
-                         "steps with chunk overlap off"),
+                         "steps with flags = 0 (every launch alone on one stream)"),
         },
         "step_ms": {"median": float(np.median(step_ms)), "min": float(min(step_ms)),
                     "max": float(max(step_ms)), "how": "HIP events between the timed steps"},
@@ -352,8 +394,7 @@ def main():
         "kernels": {
             "score": {"ms_per_step": score_ms / S, "tflops": score_tflops,
                       "mfma_frac": score_tflops / PEAK_BF16_TFLOPS},
-            "topk": {"ms_per_step": topk_ms / S, "gbs_algorithmic": topk_gbs,
-                     "hbm_frac": topk_gbs / PEAK_HBM_GBS, "launches_per_step": topk_n // S},
+            "topk": topk,
             "pool_keys": {"ms_per_step": pool_ms / S, "gbs": pool_gbs},
             "expand": {"ms_per_step": exp_ms / S, "gbs": exp_gbs},
         },
@@ -365,7 +406,8 @@ def main():
     }
     pk = probe_peaks()
     pk["score_frac_of_gemm"] = score_tflops / pk["bf16_gemm_TFLOPs"]
-    pk["topk_frac_of_copy"] = topk_gbs / pk["hbm_copy_GBs"]
+    if topk.get("achieved_GBs"):
+        pk["topk_frac_of_copy"] = topk["achieved_GBs"] / pk["hbm_copy_GBs"]
     result["probe_peaks"] = pk
     log(f"[bench] probes: copy {pk['hbm_copy_GBs']:.0f} GB/s, bf16 GEMM {pk['bf16_gemm_TFLOPs']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:

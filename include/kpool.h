@@ -33,12 +33,14 @@
  *     in kpool_last_error() (thread-local).  Nothing is thrown across the ABI.
  *     Launch failures map to KPOOL_EHIP; faults that happen while a kernel
  *     runs surface at the caller's next synchronisation.
- *   - Calls on one stream are ordered.  The library's only global state is
- *     the optional profiler below and, per device, one helper stream (default
- *     priority) with two events that kpool_score_topk uses to overlap chunks;
- *     they are created on first use and live until the process ends.  The
- *     helper joins back into the caller's stream before the call returns, so
- *     results are ordered on the caller's stream as usual.
+ *   - Every setting is an argument: there is no process-wide switch.  Calls on
+ *     one stream are ordered.  The library's only lasting state is, per caller
+ *     stream that asked for the chunk overlap (KPOOL_FLAG_OVERLAP), one helper
+ *     stream (default priority) with two events, created on first use and kept
+ *     until the process ends; the helper joins back into the caller's stream
+ *     before the call returns, so results are ordered on the caller's stream as
+ *     usual.  Calls on different caller streams use different helpers.  The
+ *     optional profiler below is per host thread.
  */
 #ifndef KPOOL_H
 #define KPOOL_H
@@ -61,7 +63,7 @@ typedef enum {
 /* Message for the last non-OK return on this thread ("" if none). */
 const char *kpool_last_error(void);
 
-/* ABI version (major*100 + minor). */
+/* ABI version (major*100 + minor): 200. */
 int kpool_version(void);
 
 /* Pool bookkeeping on the host (Atlas tp.rs module doc: a sequence of L
@@ -85,22 +87,16 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host,
 
 /* Workspace for kpool_score_topk over rows [q_lo, q_hi): per query row of a
  * chunk, one fp32 score row at a pitch of max_pools rounded up to 64 plus one
- * fp32 maximum per 16 pools of it; the score rows of a chunk are capped at
+ * fp32 maximum per 16 pools of it; the score rows of one chunk are capped at
  * 2 GiB (Megatron-LM PR #8299 "Change": the chunked score path caps its score
- * buffer at 2 GiB).  The size returned covers two such chunks when the range
- * needs more than one, so that chunks can alternate between two buffers (see
- * kpool_set_overlap).  Returns 0 for an empty range. */
-size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools);
+ * buffer at 2 GiB per chunk).  With nbuf = 2 the size covers two such chunk
+ * buffers when the range needs more than one chunk (for KPOOL_FLAG_OVERLAP:
+ * two chunks are then in flight, up to 2 x 2 GiB of scores); with nbuf = 1, one.
+ * Returns 0 for an empty range or an nbuf other than 1 or 2. */
+size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools, int32_t nbuf);
 
-/* Process-wide switch for the chunk overlap of kpool_score_topk (default on).
- * On: a workspace of two rows or more is split into two chunk buffers and
- * consecutive chunks alternate between the caller's stream and the helper
- * stream, so one chunk's selection runs beside the next chunk's scoring.
- * Off: one buffer, every launch on the caller's stream, one after the other
- * (each kernel then runs alone, which per-kernel timing needs).  Results are
- * the same either way.  Takes effect at the next kpool_score_topk call;
- * returns the previous setting (0 or 1). */
-int kpool_set_overlap(int on);
+/* Flags of kpool_score_topk. */
+#define KPOOL_FLAG_OVERLAP 1u /* two chunk buffers, chunks alternating between two streams */
 
 /* Step 2 - score and select, for the global rows [q_lo, q_hi).
  * (Megatron-LM PR #8299 "Change": one rank's contiguous slice of query rows
@@ -113,12 +109,17 @@ int kpool_set_overlap(int on);
  *   budget   pools kept per row, 1..2048 (index_topk / kpool; 2048 for the per-token
  *            indexer, kpool = 1)
  *   workspace, workspace_bytes: device scratch of at least one row
- *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools)).  With the
- *            overlap on (kpool_set_overlap), a workspace of two rows or more is
- *            split into two chunk buffers and chunks alternate between the
- *            caller's stream and the helper stream; each chunk has as many rows
- *            as the 2 GiB score cap and its buffer allow.  Contents are scratch
- *            on return.
+ *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools, 1)).  Each chunk
+ *            has as many rows as the 2 GiB score cap and its buffer allow.
+ *            Contents are scratch on return.
+ *   flags    0 or KPOOL_FLAG_OVERLAP.  0: one chunk buffer; every launch on the
+ *            caller's stream, one after the other (each kernel runs alone, which
+ *            per-kernel timing needs).  KPOOL_FLAG_OVERLAP: a workspace of two
+ *            rows or more is split into two chunk buffers, and consecutive chunks
+ *            alternate between the caller's stream and its helper stream, so one
+ *            chunk's selection runs beside the next chunk's scoring; each buffer
+ *            keeps the 2 GiB cap.  Results are bitwise the same either way.
+ *            Unknown bits return KPOOL_EINVAL.
  *   pool_ids int32 [q_hi - q_lo, budget] output: sequence-local pool ids,
  *            best first by (score desc, pool asc), -1 after the visible pools
  *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.  q, kp and
@@ -133,7 +134,7 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
                      const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                      int32_t nseq, int32_t H, int32_t D, int32_t kpool, float scale,
                      int64_t q_lo, int64_t q_hi, int32_t budget,
-                     void *workspace, size_t workspace_bytes,
+                     void *workspace, size_t workspace_bytes, uint32_t flags,
                      int32_t *pool_ids, float *scores_out, void *stream);
 
 /* Step 3 - expansion and causal filter (Megatron-LM PR #8299 "Change": pool
@@ -157,11 +158,14 @@ int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host,
 int kpool_topk(const float *scores, int64_t ld, const int32_t *n_valid, int64_t rows,
                int32_t budget, int32_t *pool_ids, void *stream);
 
-/* Optional per-kernel device timing.  While enabled, every launch made by the
- * library is bracketed by HIP events on its stream.  kpool_profile_collect
- * waits for the recorded events, adds each kernel kind's elapsed time (ms)
- * and launch count into ms[kind] / launches[kind] (arrays of
- * KPOOL_PROFILE_KINDS) and forgets the records.  Not thread-safe. */
+/* Optional per-kernel device timing, per host thread.  While enabled on a
+ * thread, every launch that thread's calls make is bracketed by HIP events on
+ * its stream.  kpool_profile_collect waits for the events the calling thread
+ * recorded, adds each kernel kind's elapsed time (ms) and launch count into
+ * ms[kind] / launches[kind] (arrays of KPOOL_PROFILE_KINDS) and forgets them.
+ * Other threads' records and switches are untouched.  Event spans of
+ * overlapped chunks (KPOOL_FLAG_OVERLAP) include whatever else the GPU runs
+ * meanwhile; time kernels with flags = 0. */
 #define KPOOL_PROFILE_KINDS 5 /* 0 pool_keys, 1 score, 2 topk, 3 expand, 4 scores_out copy */
 int kpool_profile_enable(int on);
 int kpool_profile_collect(double *ms, int64_t *launches);

@@ -10,8 +10,8 @@
 #include <stdio.h>
 
 #include <algorithm>
-#include <atomic>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -64,14 +64,16 @@ int check_cu(const int32_t *cu, int32_t nseq, const char *fn) {
 }
 
 // ---------------------------------------------------------------------------
-// Optional per-kernel timing with HIP events on the launch stream.
+// Optional per-kernel timing with HIP events on the launch stream.  The switch
+// and the records are per host thread, so one thread's profiling never sees or
+// changes another thread's launches.
 // ---------------------------------------------------------------------------
 struct ProfRec {
   int kind;
   hipEvent_t a, b;
 };
-bool g_prof_on = false;
-std::vector<ProfRec> g_prof;
+thread_local bool g_prof_on = false;
+thread_local std::vector<ProfRec> g_prof;
 
 template <class F>
 hipError_t timed(int kind, hipStream_t stream, F &&launch) {
@@ -93,34 +95,38 @@ int hip_fail(const char *fn, hipError_t e) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-device helper stream and fork/join events for the two-buffer chunk loop.
-// Created on first use (default priority, non-blocking) and kept until the
-// process ends; g_aux_mu serialises their use across host threads.
+// Helper streams for the two-buffer chunk loop: one per caller stream (so calls
+// on independent caller streams never queue behind each other), each with its
+// own fork/join events and lock.  Created on first use (default priority,
+// non-blocking) on the caller stream's device and kept until the process ends.
 // ---------------------------------------------------------------------------
 struct Aux {
+  std::mutex mu;  // held while a call enqueues on this helper
   hipStream_t helper = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
-std::mutex g_aux_mu;
-std::map<int, Aux> g_aux;
-std::atomic<int> g_overlap{1};  // process-wide: two chunk buffers on two streams
+std::mutex g_aux_mu;  // guards the map only
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Aux>> g_aux;
 
 hipError_t get_aux(hipStream_t stream, Aux **out) {
   int dev = 0;
   hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  Aux &a = g_aux[dev];
-  if (!a.helper) {
+  std::lock_guard<std::mutex> guard(g_aux_mu);
+  std::unique_ptr<Aux> &slot = g_aux[{dev, stream}];
+  if (!slot) {
+    std::unique_ptr<Aux> a(new Aux);
     int cur = 0;
     e = hipGetDevice(&cur);
     if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&a.helper, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&a.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&a.join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->helper, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a->join, hipEventDisableTiming);
     if (cur != dev) (void)hipSetDevice(cur);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) return e;  // (a partly made helper is dropped; the next call retries)
+    slot = std::move(a);
   }
-  *out = &a;
+  *out = slot.get();
   return hipSuccess;
 }
 
@@ -130,7 +136,7 @@ extern "C" {
 
 const char *kpool_last_error(void) { return g_err.c_str(); }
 
-int kpool_version(void) { return 100; }
+int kpool_version(void) { return 200; }
 
 int64_t kpool_count_pools(const int32_t *cu_seqlens_host, int32_t nseq, int32_t kpool,
                           int32_t *cu_pools_host, int32_t *max_pools_out) {
@@ -176,21 +182,19 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host, const int
 // Per row of a chunk the workspace holds ld fp32 scores and ld/16 fp32 group maxima.
 int64_t ws_row_bytes(int64_t ld) { return (ld + ld / kpool::kGroup) * 4; }
 
-size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools) {
-  if (q_hi <= q_lo || max_pools <= 0) return 0;
+size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools, int32_t nbuf) {
+  if (q_hi <= q_lo || max_pools <= 0 || (nbuf != 1 && nbuf != 2)) return 0;
   const int64_t ld = pitch_of(max_pools);
   const int64_t cap_rows = std::max<int64_t>(1, kChunkCapBytes / (ld * 4));
-  // two full chunk buffers when the rows need more than one chunk
-  return (size_t)(std::min<int64_t>(q_hi - q_lo, 2 * cap_rows) * ws_row_bytes(ld));
+  // nbuf full chunk buffers when the rows need more than one chunk
+  return (size_t)(std::min<int64_t>(q_hi - q_lo, nbuf * cap_rows) * ws_row_bytes(ld));
 }
-
-int kpool_set_overlap(int on) { return g_overlap.exchange(on ? 1 : 0); }
 
 int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
                      const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev, int32_t nseq,
                      int32_t H, int32_t D, int32_t kpool, float scale, int64_t q_lo, int64_t q_hi,
-                     int32_t budget, void *workspace, size_t workspace_bytes, int32_t *pool_ids,
-                     float *scores_out, void *stream) {
+                     int32_t budget, void *workspace, size_t workspace_bytes, uint32_t flags,
+                     int32_t *pool_ids, float *scores_out, void *stream) {
   const char *fn = "kpool_score_topk";
   int rc = check_cu(cu_seqlens_host, nseq, fn);
   if (rc) return rc;
@@ -204,6 +208,8 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
                 (long long)q_lo, (long long)q_hi, (long long)T);
   if (!kpool::score_supported(H, D))
     return fail(KPOOL_EUNSUPPORTED, "%s: (H=%d, D=%d) not compiled; supported (4,16) and (32,128)", fn, H, D);
+  if (flags & ~(uint32_t)KPOOL_FLAG_OVERLAP)
+    return fail(KPOOL_EINVAL, "%s: unknown flags 0x%x", fn, flags & ~(uint32_t)KPOOL_FLAG_OVERLAP);
   if (q_lo == q_hi) return ok();
   if (!q || !kp || !w || !cu_seqlens_dev || !pool_ids) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
   if (!aligned16(q) || !aligned16(kp) || !aligned16(w))
@@ -225,11 +231,11 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
     return fail(KPOOL_EWORKSPACE, "%s: workspace must hold one score row (%lld bytes), got %zu", fn,
                 (long long)row_bytes, workspace_bytes);
   if (!aligned16(workspace)) return fail(KPOOL_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-  // Two chunk buffers when the workspace holds at least two rows: chunks then alternate
-  // between the caller's stream and a helper stream, so one chunk's selection and the
-  // next chunk's scoring overlap instead of draining the GPU between launches.  Each
-  // buffer's fp32 score rows stay within the 2 GiB cap.
-  const int nbuf = (g_overlap.load() && (int64_t)workspace_bytes >= 2 * row_bytes) ? 2 : 1;
+  // With KPOOL_FLAG_OVERLAP and a workspace of at least two rows, two chunk buffers:
+  // chunks then alternate between the caller's stream and a helper stream, so one
+  // chunk's selection and the next chunk's scoring overlap instead of draining the GPU
+  // between launches.  Each buffer's fp32 score rows stay within the 2 GiB cap.
+  const int nbuf = ((flags & KPOOL_FLAG_OVERLAP) && (int64_t)workspace_bytes >= 2 * row_bytes) ? 2 : 1;
   const int64_t chunk_rows = std::max<int64_t>(
       1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / nbuf / row_bytes));
   const int64_t nchunks = (q_hi - q_lo + chunk_rows - 1) / chunk_rows;
@@ -304,10 +310,10 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
   }
   // chunk c goes to buffer c % 2 on stream c % 2; chunk c + 2 reuses the buffer after
   // chunk c's selection because both sit on the same stream
-  std::lock_guard<std::mutex> guard(g_aux_mu);
   Aux *aux = nullptr;
   hipError_t e = get_aux(st, &aux);
   if (e != hipSuccess) return hip_fail(fn, e);
+  std::lock_guard<std::mutex> guard(aux->mu);
   hipStream_t streams[2] = {st, aux->helper};
   e = hipEventRecord(aux->fork, st);
   if (e == hipSuccess) e = hipStreamWaitEvent(aux->helper, aux->fork, 0);

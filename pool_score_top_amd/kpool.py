@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkpool.so")
 
 KPOOL_OK, KPOOL_EINVAL, KPOOL_EUNSUPPORTED, KPOOL_EWORKSPACE, KPOOL_EHIP = 0, -1, -2, -3, -4
+KPOOL_FLAG_OVERLAP = 1
 PROFILE_KINDS = ("pool_keys", "score", "topk", "expand", "scores_copy")
 
 _lib = None
@@ -42,10 +43,9 @@ def lib():
         "kpool_version": (ctypes.c_int, []),
         "kpool_count_pools": (i64, [vp, i32, i32, vp, vp]),
         "kpool_pool_keys": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
-        "kpool_workspace_bytes": (sz, [i64, i64, i32]),
-        "kpool_set_overlap": (ctypes.c_int, [ctypes.c_int]),
+        "kpool_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "kpool_score_topk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i64, i64,
-                                            i32, vp, sz, vp, vp, vp]),
+                                            i32, vp, sz, ctypes.c_uint32, vp, vp, vp]),
         "kpool_expand": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, i64, i32, vp, vp]),
         "kpool_topk": (ctypes.c_int, [vp, i64, vp, i64, i32, vp, vp]),
         "kpool_profile_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -79,6 +79,18 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the wrappers allocate: the stream the library call will run on.
+
+    torch's caching allocator hands a freed block out again only to work ordered
+    after the frees on the block's own stream; allocating on the call's stream
+    keeps a workspace or output from being reused while the call still uses it."""
+    import contextlib
+
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _need(t, name, elem_size=None, dtype=None):
     if t is None:
         raise ValueError(f"{name} is required")
@@ -110,14 +122,10 @@ def count_pools(cu_seqlens, kpool: int):
     return out, int(mx.value), int(tot)
 
 
-def workspace_bytes(q_lo: int, q_hi: int, max_pools: int) -> int:
-    return int(lib().kpool_workspace_bytes(q_lo, q_hi, max_pools))
-
-
-def set_overlap(on: bool) -> bool:
-    """Process-wide chunk overlap of score_topk (two buffers on two streams); returns
-    the previous setting.  Off serialises every launch on the caller's stream."""
-    return bool(lib().kpool_set_overlap(1 if on else 0))
+def workspace_bytes(q_lo: int, q_hi: int, max_pools: int, nbuf: int = 2) -> int:
+    """Workspace of score_topk over rows [q_lo, q_hi): nbuf chunk buffers (2 for the
+    chunk overlap, 1 without), each capped at 2 GiB of fp32 scores."""
+    return int(lib().kpool_workspace_bytes(q_lo, q_hi, max_pools, nbuf))
 
 
 def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None, stream=None):
@@ -128,7 +136,8 @@ def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None,
     _, _, P_tot = count_pools(cu, kpool)
     D = k.shape[-1]
     if out is None:
-        out = torch.empty((P_tot, D), dtype=k.dtype, device=k.device)
+        with _on(stream):
+            out = torch.empty((P_tot, D), dtype=k.dtype, device=k.device)
     rc = lib().kpool_pool_keys(_p(k), cup, _p(cu_seqlens_dev), _p(cu_pools_dev), nseq, D, kpool,
                                _p(out), _stream(stream))
     _check(rc, "kpool_pool_keys")
@@ -137,8 +146,12 @@ def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None,
 
 def score_topk(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_lo: int = 0,
                q_hi: int | None = None, scale: float | None = None, workspace=None,
-               pool_ids=None, scores_out=None, want_scores: bool = False, stream=None):
-    """Run the chunked score + top-k for rows [q_lo, q_hi).  Returns (pool_ids, scores_out)."""
+               pool_ids=None, scores_out=None, want_scores: bool = False, overlap: bool = False,
+               stream=None):
+    """Run the chunked score + top-k for rows [q_lo, q_hi).  Returns (pool_ids, scores_out).
+
+    overlap=True passes KPOOL_FLAG_OVERLAP (two chunk buffers on two streams); a
+    workspace allocated here then holds two chunk buffers, otherwise one."""
     import torch
     _need(q, "q", 2)
     _need(kp, "kp", 2)
@@ -153,16 +166,18 @@ def score_topk(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_
         scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
     _, max_pools, _ = count_pools(cu, kpool)
     rows = max(0, q_hi - q_lo)
-    if pool_ids is None:
-        pool_ids = torch.empty((rows, budget), dtype=torch.int32, device=q.device)
-    if want_scores and scores_out is None:
-        scores_out = torch.empty((rows, max_pools), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        nb = workspace_bytes(q_lo, q_hi, max_pools)
-        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if pool_ids is None:
+            pool_ids = torch.empty((rows, budget), dtype=torch.int32, device=q.device)
+        if want_scores and scores_out is None:
+            scores_out = torch.empty((rows, max_pools), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            nb = workspace_bytes(q_lo, q_hi, max_pools, 2 if overlap else 1)
+            workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
     rc = lib().kpool_score_topk(_p(q), _p(kp), _p(w), cup, _p(cu_seqlens_dev), nseq, H, D, kpool,
                                 ctypes.c_float(scale), q_lo, q_hi, budget, _p(workspace),
-                                workspace.numel() * workspace.element_size(), _p(pool_ids),
+                                workspace.numel() * workspace.element_size(),
+                                KPOOL_FLAG_OVERLAP if overlap else 0, _p(pool_ids),
                                 _p(scores_out), _stream(stream))
     _check(rc, "kpool_score_topk")
     return pool_ids, scores_out
@@ -177,7 +192,8 @@ def expand(pool_ids, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_lo: 
         q_hi = int(cu[-1])
     rows = max(0, q_hi - q_lo)
     if out is None:
-        out = torch.empty((rows, budget * kpool), dtype=torch.int32, device=pool_ids.device)
+        with _on(stream):
+            out = torch.empty((rows, budget * kpool), dtype=torch.int32, device=pool_ids.device)
     rc = lib().kpool_expand(_p(pool_ids), cup, _p(cu_seqlens_dev), nseq, kpool, q_lo, q_hi, budget,
                             _p(out), _stream(stream))
     _check(rc, "kpool_expand")
@@ -190,7 +206,8 @@ def topk(scores, n_valid, budget: int, out=None, stream=None):
     _need(scores, "scores", dtype=torch.float32)
     rows, ld = scores.shape
     if out is None:
-        out = torch.empty((rows, budget), dtype=torch.int32, device=scores.device)
+        with _on(stream):
+            out = torch.empty((rows, budget), dtype=torch.int32, device=scores.device)
     rc = lib().kpool_topk(_p(scores), ld, _p(n_valid), rows, budget, _p(out), _stream(stream))
     _check(rc, "kpool_topk")
     return out
@@ -217,22 +234,26 @@ class Selector:
 
     Holds the device copies of cu_seqlens / cu_pools and a workspace sized
     for the row range; `run` enqueues the three library calls on one stream.
+    overlap=True (the default) sizes the workspace for two chunk buffers and runs
+    the chunk loop with KPOOL_FLAG_OVERLAP; workspace_cap caps the workspace
+    (smaller chunks).
     """
 
     def __init__(self, cu_seqlens, kpool: int, budget: int, H: int, D: int, device="cuda",
                  q_lo: int = 0, q_hi: int | None = None, workspace_cap: int | None = None,
-                 scale: float | None = None):
+                 scale: float | None = None, overlap: bool = True):
         import torch
         self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
         self.T = int(self.cu[-1])
         self.kpool, self.budget, self.H, self.D = kpool, budget, H, D
         self.q_lo = q_lo
         self.q_hi = self.T if q_hi is None else q_hi
+        self.overlap = overlap
         self.cu_pools, self.max_pools, self.P_tot = count_pools(self.cu, kpool)
         self.cu_dev = torch.from_numpy(self.cu).to(device)
         self.cu_pools_dev = torch.from_numpy(self.cu_pools).to(device)
         self.scale = float(np.float32(1.0) / np.sqrt(np.float32(D))) if scale is None else scale
-        nb = workspace_bytes(self.q_lo, self.q_hi, self.max_pools)
+        nb = workspace_bytes(self.q_lo, self.q_hi, self.max_pools, 2 if overlap else 1)
         if workspace_cap is not None:
             nb = min(nb, workspace_cap)
         self.workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)
@@ -241,11 +262,24 @@ class Selector:
         self.pool_ids = torch.empty((rows, budget), dtype=torch.int32, device=device)
         self.token_ids = torch.empty((rows, budget * kpool), dtype=torch.int32, device=device)
 
-    def run(self, q, k, w, scores_out=None, stream=None):
+    @property
+    def workspace_bytes(self) -> int:
+        return self.workspace.numel()
+
+    def chunk_rows(self, overlap: bool | None = None) -> int:
+        """Rows per chunk of the chunk loop with this workspace (as the library plans it)."""
+        overlap = self.overlap if overlap is None else overlap
+        ld = (self.max_pools + 63) // 64 * 64
+        row_bytes = (ld + ld // 16) * 4
+        nbuf = 2 if overlap and self.workspace_bytes >= 2 * row_bytes else 1
+        return max(1, min((1 << 31) // (ld * 4), self.workspace_bytes // nbuf // row_bytes))
+
+    def run(self, q, k, w, scores_out=None, stream=None, overlap: bool | None = None):
+        overlap = self.overlap if overlap is None else overlap
         pool_keys(k, self.cu, self.cu_dev, self.cu_pools_dev, self.kpool, out=self.kp, stream=stream)
         score_topk(q, self.kp, w, self.cu, self.cu_dev, self.kpool, self.budget, self.q_lo, self.q_hi,
                    scale=self.scale, workspace=self.workspace, pool_ids=self.pool_ids,
-                   scores_out=scores_out, stream=stream)
+                   scores_out=scores_out, overlap=overlap, stream=stream)
         expand(self.pool_ids, self.cu, self.cu_dev, self.kpool, self.budget, self.q_lo, self.q_hi,
                out=self.token_ids, stream=stream)
         return {"kp": self.kp, "pool_ids": self.pool_ids, "token_ids": self.token_ids}

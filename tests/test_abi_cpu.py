@@ -32,17 +32,13 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(K.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(L, n)]
     assert not missing, missing
-    assert K.version() == 100
 
 
-def test_set_overlap_returns_previous_setting():
-    prev = K.set_overlap(False)
-    try:
-        assert K.set_overlap(False) is False
-        assert K.set_overlap(True) is False
-        assert K.set_overlap(True) is True
-    finally:
-        K.set_overlap(prev)
+def test_no_process_wide_switch_in_the_header():
+    """Every setting is an argument of the call: the header declares no setter."""
+    names = declared_functions()
+    assert not [n for n in names if "set_" in n], names
+    assert K.version() == 200
 
 
 def test_count_pools_and_workspace():
@@ -52,24 +48,27 @@ def test_count_pools_and_workspace():
     # plus one fp32 group maximum per 16 pools of each row; two chunk buffers when the
     # range needs more than one chunk
     assert K.workspace_bytes(0, 524288, 131072) == 2 * 4096 * (131072 + 8192) * 4
+    assert K.workspace_bytes(0, 524288, 131072, 1) == 4096 * (131072 + 8192) * 4
     assert K.workspace_bytes(0, 6000, 131072) == 6000 * (131072 + 8192) * 4
+    assert K.workspace_bytes(0, 6000, 131072, 1) == 4096 * (131072 + 8192) * 4
     assert K.workspace_bytes(0, 100, 131072) == 100 * (131072 + 8192) * 4
     assert K.workspace_bytes(5, 5, 10) == 0
     assert K.workspace_bytes(0, 3, 1) == 3 * (64 + 4) * 4   # pitch rounds up to 64
+    assert K.workspace_bytes(0, 3, 1, 0) == 0 and K.workspace_bytes(0, 3, 1, 3) == 0
 
 
 def _call_score(**kw):
     L = K.lib()
     cu = np.array(kw.pop("cu", [0, 64]), dtype=np.int32)
     args = dict(q=16, kp=16, w=16, cu_dev=16, nseq=len(cu) - 1, H=4, D=16, kpool=4, scale=0.25,
-                q_lo=0, q_hi=int(cu[-1]), budget=4, ws=16, ws_bytes=1 << 20, ids=16)
+                q_lo=0, q_hi=int(cu[-1]), budget=4, ws=16, ws_bytes=1 << 20, flags=0, ids=16)
     args.update(kw)
     vp = ctypes.c_void_p
     return L.kpool_score_topk(vp(args["q"]), vp(args["kp"]), vp(args["w"]),
                               cu.ctypes.data_as(vp), vp(args["cu_dev"]), args["nseq"], args["H"],
                               args["D"], args["kpool"], ctypes.c_float(args["scale"]), args["q_lo"],
                               args["q_hi"], args["budget"], vp(args["ws"]), args["ws_bytes"],
-                              vp(args["ids"]), None, None)
+                              args["flags"], vp(args["ids"]), None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -90,6 +89,8 @@ def _call_score(**kw):
     (dict(cu=[1, 64]), K.KPOOL_EINVAL),
     (dict(cu=[0, 40, 30, 64]), K.KPOOL_EINVAL),
     (dict(nseq=0), K.KPOOL_EINVAL),
+    (dict(flags=2), K.KPOOL_EINVAL),         # unknown flag bit
+    (dict(flags=0x80000001), K.KPOOL_EINVAL),
     # one sequence whose pooled keys exceed the kernel's 32-bit byte offsets (2^24 pools at D=128)
     (dict(cu=[0, 1 << 24], kpool=1, H=32, D=128), K.KPOOL_EUNSUPPORTED),
 ])
@@ -120,18 +121,3 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.kpool_topk(vp(8), 8, vp(16), 3, 4, vp(16), None) == K.KPOOL_EINVAL       # alignment
     assert L.kpool_topk(None, 8, vp(16), 0, 4, None, None) == K.KPOOL_OK              # no rows
     assert L.kpool_count_pools(cup, 1, 0, None, None) == K.KPOOL_EINVAL
-
-
-def test_shard_bounds_cover_every_row_once():
-    """The pages' per-rank bounds [r*ceil(sq/G), min(sq, (r+1)*ceil(sq/G))) partition the rows
-    (Megatron-LM PR #8299, 'Change' and 'Test plan'); the one-GPU row ranges use the same
-    arithmetic, including empty ranges when sq < G."""
-    for sq in (5, 24, 37, 4096):
-        for G in (1, 2, 3, 8):
-            per = -(-sq // G)
-            seen = np.zeros(sq, dtype=np.int64)
-            for r in range(G):
-                lo, hi = min(sq, r * per), min(sq, (r + 1) * per)
-                assert lo <= hi
-                seen[lo:hi] += 1
-            assert np.all(seen == 1)

@@ -44,22 +44,42 @@ def test_visible_pairs_closed_forms():
     assert bench.visible_pairs(np.array([0, 524288]), 458752, 524288, 4) == full - head == 8053096448
 
 
-def test_traffic_figure_goes_stale_with_the_kernel(tmp_path, monkeypatch):
-    """The committed FETCH/WRITE figure is used only while score.hip and api.hip hash
-    to the values it was measured on."""
-    prof = os.path.join(bench.ROOT, "profiles", "score_kernel_sq524288_traffic.md")
-    if not os.path.exists(prof):
-        pytest.skip("no committed traffic summary")
+def _fake_repo(tmp_path, with_hashes=True):
+    import hashlib
     root = tmp_path / "repo"
     (root / "profiles").mkdir(parents=True)
-    shutil.copytree(os.path.join(bench.ROOT, "pool_score_top_amd", "csrc"),
-                    root / "pool_score_top_amd" / "csrc")
-    shutil.copy(prof, root / "profiles")
+    csrc = root / "pool_score_top_amd" / "csrc"
+    shutil.copytree(os.path.join(bench.ROOT, "pool_score_top_amd", "csrc"), csrc)
+    lines = ["# counters", "```"]
+    for name in bench.COUNTER_SOURCES:
+        sha = hashlib.sha256((csrc / name).read_bytes()).hexdigest() if with_hashes else "0" * 64
+        lines.append(f"sha256_{name}: {sha}")
+    lines += ["score_fetch_bytes_per_launch: 341156430", "score_write_bytes_per_launch: 1174277950",
+              "score_mfma_busy_frac: 0.716", "topk_fetch_bytes_per_launch: 404000000",
+              "topk_write_bytes_per_launch: 8400000", "```"]
+    (root / "profiles" / "counters_sqX.md").write_text("\n".join(lines) + "\n")
+    return root
+
+
+def test_counter_figures_go_stale_with_the_sources(tmp_path, monkeypatch):
+    """Committed counter figures are used only while score.hip, topk.hip and api.hip hash
+    to the values they were measured on."""
+    root = _fake_repo(tmp_path)
     monkeypatch.setattr(bench, "ROOT", str(root))
-    t = bench.score_traffic("sq524288")
-    if t is not None:  # the summary matches the sources: a changed kernel must void it
-        assert t["fetch"] > 0 and t["write"] > 0
-    with open(root / "pool_score_top_amd" / "csrc" / "score.hip", "a") as f:
-        f.write("\n// changed\n")
-    assert bench.score_traffic("sq524288") is None
-    assert bench.score_traffic("no_such_workload") is None
+    c = bench.committed_counters("sqX")
+    assert c["score_fetch_bytes_per_launch"] == 341156430 and c["topk_write_bytes_per_launch"] == 8.4e6
+    assert c["score_mfma_busy_frac"] == 0.716
+    assert bench.committed_counters("no_such_workload") is None
+    for name in bench.COUNTER_SOURCES:
+        f = root / "pool_score_top_amd" / "csrc" / name
+        orig = f.read_bytes()
+        f.write_bytes(orig + b"\n// changed\n")
+        assert bench.committed_counters("sqX") is None, name
+        f.write_bytes(orig)
+    assert bench.committed_counters("sqX") is not None
+
+
+def test_counter_figures_with_wrong_hashes_are_ignored(tmp_path, monkeypatch):
+    root = _fake_repo(tmp_path, with_hashes=False)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    assert bench.committed_counters("sqX") is None

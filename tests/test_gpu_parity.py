@@ -191,12 +191,8 @@ def test_row_split_and_chunking_reassemble_bitwise(kpool, budget):
                  for a, b in zip(bounds[:-1], bounds[1:])]
         for key in ("pool_ids", "token_ids", "scores"):
             np.testing.assert_array_equal(np.concatenate([p[key] for p in parts]), full[key], err_msg=key)
-    # the same chunks serialised on one stream (overlap off) give the same bits
-    prev = K.set_overlap(False)
-    try:
-        serial = run_gpu(r, wl.kpool, budget, workspace_cap=7 * row_bytes)
-    finally:
-        K.set_overlap(prev)
+    # the same chunks serialised on one stream (flags = 0) give the same bits
+    serial = run_gpu(r, wl.kpool, budget, workspace_cap=7 * row_bytes, overlap=False)
     for key in ("pool_ids", "token_ids", "scores"):
         np.testing.assert_array_equal(serial[key], full[key], err_msg=key)
 
