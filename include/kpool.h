@@ -137,6 +137,27 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
                      void *workspace, size_t workspace_bytes, uint32_t flags,
                      int32_t *pool_ids, float *scores_out, void *stream);
 
+/* kpool_score_topk for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.  Same
+ * arguments and results as kpool_score_topk with flags = 0, but the workspace is a
+ * static device array of KPOOL_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library:
+ * each GPU the library runs on holds its own copy until the process ends.  The call
+ * allocates nothing (no hipMalloc / hipFree, no stream or event creation; the profiler
+ * is bypassed); its chunks, as many rows each as one 64 MiB workspace holds, run on
+ * `stream` one after the other.
+ *   - A sequence whose score row (its pools rounded up to 64, plus one maximum per
+ *     16 of them, 4 bytes each) exceeds the scratch, i.e. more than about 15.79M
+ *     pools, returns KPOOL_EWORKSPACE with a message saying so.
+ *   - All calls on one GPU share that GPU's array, which keeps the last call's
+ *     contents (nothing in it needs clearing between calls).  Calls that overlap on
+ *     one GPU (different streams or host threads at once) race on it: order them. */
+#define KPOOL_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kpool_score_topk_noalloc(const uint16_t *q, const uint16_t *kp, const float *w,
+                             const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                             int32_t nseq, int32_t H, int32_t D, int32_t kpool, float scale,
+                             int64_t q_lo, int64_t q_hi, int32_t budget, int32_t *pool_ids,
+                             float *scores_out, void *stream);
+
 /* Step 3 - expansion and causal filter (Megatron-LM PR #8299 "Change": pool
  * expansion and mask filtering run after the pool ids are known).
  *   token_ids[i - q_lo, b*kpool + j] = p*kpool + j   if p = pool_ids[i - q_lo, b] >= 0

@@ -90,6 +90,11 @@ hipError_t timed(int kind, hipStream_t stream, F &&launch) {
   return e;
 }
 
+template <class F>
+hipError_t timed_if(bool profile, int kind, hipStream_t stream, F &&launch) {
+  return profile ? timed(kind, stream, launch) : launch();
+}
+
 int hip_fail(const char *fn, hipError_t e) {
   return fail(KPOOL_EHIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
 }
@@ -128,6 +133,198 @@ hipError_t get_aux(hipStream_t stream, Aux **out) {
   }
   *out = slot.get();
   return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for kpool_score_topk_noalloc: the chunk workspace of callers that
+// cannot allocate device memory.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` is only a host-side stand-in for the
+// symbol; the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is handed to kernels.  Nothing in it
+// has to start at zero: each chunk's score kernel writes every score and group maximum
+// that the chunk's selection then reads.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = KPOOL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_ptr(hipStream_t stream, void **out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void *p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Per row of a chunk the workspace holds ld fp32 scores and ld/16 fp32 group maxima.
+int64_t ws_row_bytes(int64_t ld) { return (ld + ld / kpool::kGroup) * 4; }
+// The chunk loop behind kpool_score_topk and kpool_score_topk_noalloc.  With
+// use_scratch, the workspace is this device's static scratch array (resolved after the
+// arguments are validated), chunks run on the caller's stream one after the other and
+// the profiler is bypassed, so the call creates and allocates nothing.
+int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const float *w,
+                    const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev, int32_t nseq,
+                    int32_t H, int32_t D, int32_t kpool, float scale, int64_t q_lo, int64_t q_hi,
+                    int32_t budget, void *workspace, size_t workspace_bytes, uint32_t flags,
+                    bool use_scratch, int32_t *pool_ids, float *scores_out, void *stream) {
+  int rc = check_cu(cu_seqlens_host, nseq, fn);
+  if (rc) return rc;
+  const int64_t T = cu_seqlens_host[nseq];
+  if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
+  if (budget < 1 || budget > kpool::kTopkMaxBudget)
+    return fail(KPOOL_EINVAL, "%s: budget must be in [1, %d] (got %d)", fn, kpool::kTopkMaxBudget, budget);
+  if (!(scale > 0.0f) || !isfinite(scale)) return fail(KPOOL_EINVAL, "%s: scale must be finite and > 0", fn);
+  if (q_lo < 0 || q_lo > q_hi || q_hi > T)
+    return fail(KPOOL_EINVAL, "%s: need 0 <= q_lo <= q_hi <= T (q_lo=%lld q_hi=%lld T=%lld)", fn,
+                (long long)q_lo, (long long)q_hi, (long long)T);
+  if (!kpool::score_supported(H, D))
+    return fail(KPOOL_EUNSUPPORTED, "%s: (H=%d, D=%d) not compiled; supported (4,16) and (32,128)", fn, H, D);
+  if (flags & ~(uint32_t)KPOOL_FLAG_OVERLAP)
+    return fail(KPOOL_EINVAL, "%s: unknown flags 0x%x", fn, flags & ~(uint32_t)KPOOL_FLAG_OVERLAP);
+  if (q_lo == q_hi) return ok();
+  if (!q || !kp || !w || !cu_seqlens_dev || !pool_ids) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
+  if (!aligned16(q) || !aligned16(kp) || !aligned16(w))
+    return fail(KPOOL_EINVAL, "%s: q, kp and w must be 16-byte aligned", fn);
+
+  std::vector<int32_t> cu_pools(nseq + 1);
+  int32_t max_pools = 0;
+  kpool_count_pools(cu_seqlens_host, nseq, kpool, cu_pools.data(), &max_pools);
+  // The score kernel addresses one sequence's pooled keys and one chunk's score rows
+  // with 32-bit byte offsets: a sequence's keys must stay below 4 GiB (16M pools at
+  // D = 128) and one score row within the 2 GiB chunk cap.
+  if ((int64_t)max_pools * D * 2 > (int64_t)0xFFFFFFFF || pitch_of(max_pools) * 4 > kChunkCapBytes)
+    return fail(KPOOL_EUNSUPPORTED, "%s: a sequence of %d pools is beyond the supported size", fn,
+                max_pools);
+  const int64_t ld = pitch_of(max_pools);
+  const int64_t ldg = ld / kpool::kGroup;
+  const int64_t row_bytes = ws_row_bytes(ld);
+  hipStream_t st = (hipStream_t)stream;
+  if (use_scratch) {
+    if (row_bytes > (int64_t)kScratchBytes)
+      return fail(KPOOL_EWORKSPACE,
+                  "%s: one score row needs %lld bytes, beyond the %lld-byte static scratch (a "
+                  "sequence of %d pools; at most %lld pools fit)", fn, (long long)row_bytes,
+                  (long long)kScratchBytes, max_pools, (long long)(kScratchBytes / 4 * 16 / 17));
+    hipError_t e = scratch_ptr(st, &workspace);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    workspace_bytes = kScratchBytes;
+    flags = 0;
+  }
+  if (!workspace || (int64_t)workspace_bytes < row_bytes)
+    return fail(KPOOL_EWORKSPACE, "%s: workspace must hold one score row (%lld bytes), got %zu", fn,
+                (long long)row_bytes, workspace_bytes);
+  if (!aligned16(workspace)) return fail(KPOOL_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  // With KPOOL_FLAG_OVERLAP and a workspace of at least two rows, two chunk buffers:
+  // chunks then alternate between the caller's stream and a helper stream, so one
+  // chunk's selection and the next chunk's scoring overlap instead of draining the GPU
+  // between launches.  Each buffer's fp32 score rows stay within the 2 GiB cap.
+  const int nbuf = ((flags & KPOOL_FLAG_OVERLAP) && (int64_t)workspace_bytes >= 2 * row_bytes) ? 2 : 1;
+  const int64_t chunk_rows = std::max<int64_t>(
+      1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / nbuf / row_bytes));
+  const int64_t nchunks = (q_hi - q_lo + chunk_rows - 1) / chunk_rows;
+  float *ws_buf[2], *gws_buf[2];
+  for (int b = 0; b < 2; ++b) {
+    ws_buf[b] = (float *)((char *)workspace + (b % nbuf) * chunk_rows * row_bytes);
+    gws_buf[b] = ws_buf[b] + chunk_rows * ld;  // group maxima follow the score rows
+  }
+  const int tile_rows = kpool::score_tile_rows();
+
+  // score + select of rows [c0, c1) into one buffer, on one stream
+  auto enqueue_chunk = [&](int64_t c0, int64_t c1, float *ws, float *gws, hipStream_t cs) -> hipError_t {
+    // sequences overlapping [c0, c1): one segment each, cut into row tiles
+    struct Seg { int32_t lo, hi, start, pool_base; };
+    std::vector<Seg> segs;
+    int s = (int)(std::upper_bound(cu_seqlens_host, cu_seqlens_host + nseq + 1, (int32_t)c0) -
+                  cu_seqlens_host) - 1;
+    for (; s < nseq && cu_seqlens_host[s] < c1; ++s) {
+      const int64_t lo = std::max<int64_t>(c0, cu_seqlens_host[s]);
+      const int64_t hi = std::min<int64_t>(c1, cu_seqlens_host[s + 1]);
+      if (lo < hi) segs.push_back({(int32_t)lo, (int32_t)hi, cu_seqlens_host[s], cu_pools[s]});
+    }
+    for (size_t g0 = 0; g0 < segs.size(); g0 += kpool::kMaxSegs) {
+      kpool::SegList L{};
+      int32_t ntiles = 0, max_npv = 0;
+      for (size_t g = g0; g < std::min(segs.size(), g0 + kpool::kMaxSegs); ++g) {
+        const Seg &sg = segs[g];
+        const int j = L.nseg++;
+        L.tile_start[j] = ntiles;
+        L.row_lo[j] = sg.lo;
+        L.row_hi[j] = sg.hi;
+        L.seq_start[j] = sg.start;
+        L.pool_base[j] = sg.pool_base;
+        ntiles += (sg.hi - sg.lo + tile_rows - 1) / tile_rows;
+        max_npv = std::max<int32_t>(max_npv, (sg.hi - 1 - sg.start) / kpool + 1);
+      }
+      L.tile_start[L.nseg] = ntiles;
+      // pool segments per tile: about KPOOL_SCORE_TARGET_WGS workgroups per launch (4 per
+      // CU), at most kPoolSegMax pools each; fewer, longer workgroups reload q less often
+      const int64_t want_segs =
+          std::max<int64_t>(1, (KPOOL_SCORE_TARGET_WGS + ntiles - 1) / ntiles);
+      int64_t pseg = (max_npv + want_segs - 1) / want_segs;
+      pseg = std::min<int64_t>(kPoolSegMax, std::max<int64_t>(64, (pseg + 63) / 64 * 64));
+      const int32_t npseg = (int32_t)((max_npv + pseg - 1) / pseg);
+      hipError_t e = timed_if(!use_scratch, 1, cs, [&] {
+        return kpool::launch_score(H, D, q, kp, w, scale, kpool, L, ntiles, npseg, (int32_t)pseg,
+                                   c0, ld, ws, ldg, gws, cs);
+      });
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = timed_if(!use_scratch, 2, cs, [&] {
+      return kpool::launch_topk(ws, ld, c1 - c0, nullptr, cu_seqlens_dev, nseq, c0, kpool, budget,
+                                pool_ids + (c0 - q_lo) * budget, gws, ldg, cs);
+    });
+    if (e != hipSuccess) return e;
+    if (scores_out) {
+      e = timed_if(!use_scratch, 4, cs, [&] {
+        return kpool::launch_scores_copy(ws, ld, c1 - c0, cu_seqlens_dev, nseq, c0, kpool,
+                                         scores_out + (c0 - q_lo) * max_pools, max_pools, cs);
+      });
+    }
+    return e;
+  };
+
+  if (nbuf == 1 || nchunks == 1) {
+    for (int64_t c0 = q_lo; c0 < q_hi; c0 += chunk_rows) {
+      hipError_t e = enqueue_chunk(c0, std::min(q_hi, c0 + chunk_rows), ws_buf[0], gws_buf[0], st);
+      if (e != hipSuccess) return hip_fail(fn, e);
+    }
+    return ok();
+  }
+  // chunk c goes to buffer c % 2 on stream c % 2; chunk c + 2 reuses the buffer after
+  // chunk c's selection because both sit on the same stream
+  Aux *aux = nullptr;
+  hipError_t e = get_aux(st, &aux);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  std::lock_guard<std::mutex> guard(aux->mu);
+  hipStream_t streams[2] = {st, aux->helper};
+  e = hipEventRecord(aux->fork, st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(aux->helper, aux->fork, 0);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  hipError_t first_err = hipSuccess;
+  int64_t c = 0;
+  for (int64_t c0 = q_lo; c0 < q_hi && first_err == hipSuccess; c0 += chunk_rows, ++c)
+    first_err = enqueue_chunk(c0, std::min(q_hi, c0 + chunk_rows), ws_buf[c & 1], gws_buf[c & 1],
+                              streams[c & 1]);
+  // join: the caller's stream waits for the helper whatever happened above
+  e = hipEventRecord(aux->join, aux->helper);
+  if (e == hipSuccess) e = hipStreamWaitEvent(st, aux->join, 0);
+  if (first_err != hipSuccess) return hip_fail(fn, first_err);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
 }
 
 }  // namespace
@@ -179,9 +376,6 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host, const int
   return ok();
 }
 
-// Per row of a chunk the workspace holds ld fp32 scores and ld/16 fp32 group maxima.
-int64_t ws_row_bytes(int64_t ld) { return (ld + ld / kpool::kGroup) * 4; }
-
 size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools, int32_t nbuf) {
   if (q_hi <= q_lo || max_pools <= 0 || (nbuf != 1 && nbuf != 2)) return 0;
   const int64_t ld = pitch_of(max_pools);
@@ -195,140 +389,19 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
                      int32_t H, int32_t D, int32_t kpool, float scale, int64_t q_lo, int64_t q_hi,
                      int32_t budget, void *workspace, size_t workspace_bytes, uint32_t flags,
                      int32_t *pool_ids, float *scores_out, void *stream) {
-  const char *fn = "kpool_score_topk";
-  int rc = check_cu(cu_seqlens_host, nseq, fn);
-  if (rc) return rc;
-  const int64_t T = cu_seqlens_host[nseq];
-  if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
-  if (budget < 1 || budget > kpool::kTopkMaxBudget)
-    return fail(KPOOL_EINVAL, "%s: budget must be in [1, %d] (got %d)", fn, kpool::kTopkMaxBudget, budget);
-  if (!(scale > 0.0f) || !isfinite(scale)) return fail(KPOOL_EINVAL, "%s: scale must be finite and > 0", fn);
-  if (q_lo < 0 || q_lo > q_hi || q_hi > T)
-    return fail(KPOOL_EINVAL, "%s: need 0 <= q_lo <= q_hi <= T (q_lo=%lld q_hi=%lld T=%lld)", fn,
-                (long long)q_lo, (long long)q_hi, (long long)T);
-  if (!kpool::score_supported(H, D))
-    return fail(KPOOL_EUNSUPPORTED, "%s: (H=%d, D=%d) not compiled; supported (4,16) and (32,128)", fn, H, D);
-  if (flags & ~(uint32_t)KPOOL_FLAG_OVERLAP)
-    return fail(KPOOL_EINVAL, "%s: unknown flags 0x%x", fn, flags & ~(uint32_t)KPOOL_FLAG_OVERLAP);
-  if (q_lo == q_hi) return ok();
-  if (!q || !kp || !w || !cu_seqlens_dev || !pool_ids) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
-  if (!aligned16(q) || !aligned16(kp) || !aligned16(w))
-    return fail(KPOOL_EINVAL, "%s: q, kp and w must be 16-byte aligned", fn);
+  return score_topk_impl("kpool_score_topk", q, kp, w, cu_seqlens_host, cu_seqlens_dev, nseq, H, D,
+                         kpool, scale, q_lo, q_hi, budget, workspace, workspace_bytes, flags, false,
+                         pool_ids, scores_out, stream);
+}
 
-  std::vector<int32_t> cu_pools(nseq + 1);
-  int32_t max_pools = 0;
-  kpool_count_pools(cu_seqlens_host, nseq, kpool, cu_pools.data(), &max_pools);
-  // The score kernel addresses one sequence's pooled keys and one chunk's score rows
-  // with 32-bit byte offsets: a sequence's keys must stay below 4 GiB (16M pools at
-  // D = 128) and one score row within the 2 GiB chunk cap.
-  if ((int64_t)max_pools * D * 2 > (int64_t)0xFFFFFFFF || pitch_of(max_pools) * 4 > kChunkCapBytes)
-    return fail(KPOOL_EUNSUPPORTED, "%s: a sequence of %d pools is beyond the supported size", fn,
-                max_pools);
-  const int64_t ld = pitch_of(max_pools);
-  const int64_t ldg = ld / kpool::kGroup;
-  const int64_t row_bytes = ws_row_bytes(ld);
-  if (!workspace || (int64_t)workspace_bytes < row_bytes)
-    return fail(KPOOL_EWORKSPACE, "%s: workspace must hold one score row (%lld bytes), got %zu", fn,
-                (long long)row_bytes, workspace_bytes);
-  if (!aligned16(workspace)) return fail(KPOOL_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-  // With KPOOL_FLAG_OVERLAP and a workspace of at least two rows, two chunk buffers:
-  // chunks then alternate between the caller's stream and a helper stream, so one
-  // chunk's selection and the next chunk's scoring overlap instead of draining the GPU
-  // between launches.  Each buffer's fp32 score rows stay within the 2 GiB cap.
-  const int nbuf = ((flags & KPOOL_FLAG_OVERLAP) && (int64_t)workspace_bytes >= 2 * row_bytes) ? 2 : 1;
-  const int64_t chunk_rows = std::max<int64_t>(
-      1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / nbuf / row_bytes));
-  const int64_t nchunks = (q_hi - q_lo + chunk_rows - 1) / chunk_rows;
-  float *ws_buf[2], *gws_buf[2];
-  for (int b = 0; b < 2; ++b) {
-    ws_buf[b] = (float *)((char *)workspace + (b % nbuf) * chunk_rows * row_bytes);
-    gws_buf[b] = ws_buf[b] + chunk_rows * ld;  // group maxima follow the score rows
-  }
-  hipStream_t st = (hipStream_t)stream;
-  const int tile_rows = kpool::score_tile_rows();
-
-  // score + select of rows [c0, c1) into one buffer, on one stream
-  auto enqueue_chunk = [&](int64_t c0, int64_t c1, float *ws, float *gws, hipStream_t cs) -> hipError_t {
-    // sequences overlapping [c0, c1): one segment each, cut into row tiles
-    struct Seg { int32_t lo, hi, start, pool_base; };
-    std::vector<Seg> segs;
-    int s = (int)(std::upper_bound(cu_seqlens_host, cu_seqlens_host + nseq + 1, (int32_t)c0) -
-                  cu_seqlens_host) - 1;
-    for (; s < nseq && cu_seqlens_host[s] < c1; ++s) {
-      const int64_t lo = std::max<int64_t>(c0, cu_seqlens_host[s]);
-      const int64_t hi = std::min<int64_t>(c1, cu_seqlens_host[s + 1]);
-      if (lo < hi) segs.push_back({(int32_t)lo, (int32_t)hi, cu_seqlens_host[s], cu_pools[s]});
-    }
-    for (size_t g0 = 0; g0 < segs.size(); g0 += kpool::kMaxSegs) {
-      kpool::SegList L{};
-      int32_t ntiles = 0, max_npv = 0;
-      for (size_t g = g0; g < std::min(segs.size(), g0 + kpool::kMaxSegs); ++g) {
-        const Seg &sg = segs[g];
-        const int j = L.nseg++;
-        L.tile_start[j] = ntiles;
-        L.row_lo[j] = sg.lo;
-        L.row_hi[j] = sg.hi;
-        L.seq_start[j] = sg.start;
-        L.pool_base[j] = sg.pool_base;
-        ntiles += (sg.hi - sg.lo + tile_rows - 1) / tile_rows;
-        max_npv = std::max<int32_t>(max_npv, (sg.hi - 1 - sg.start) / kpool + 1);
-      }
-      L.tile_start[L.nseg] = ntiles;
-      // pool segments per tile: about KPOOL_SCORE_TARGET_WGS workgroups per launch (4 per
-      // CU), at most kPoolSegMax pools each; fewer, longer workgroups reload q less often
-      const int64_t want_segs =
-          std::max<int64_t>(1, (KPOOL_SCORE_TARGET_WGS + ntiles - 1) / ntiles);
-      int64_t pseg = (max_npv + want_segs - 1) / want_segs;
-      pseg = std::min<int64_t>(kPoolSegMax, std::max<int64_t>(64, (pseg + 63) / 64 * 64));
-      const int32_t npseg = (int32_t)((max_npv + pseg - 1) / pseg);
-      hipError_t e = timed(1, cs, [&] {
-        return kpool::launch_score(H, D, q, kp, w, scale, kpool, L, ntiles, npseg, (int32_t)pseg,
-                                   c0, ld, ws, ldg, gws, cs);
-      });
-      if (e != hipSuccess) return e;
-    }
-    hipError_t e = timed(2, cs, [&] {
-      return kpool::launch_topk(ws, ld, c1 - c0, nullptr, cu_seqlens_dev, nseq, c0, kpool, budget,
-                                pool_ids + (c0 - q_lo) * budget, gws, ldg, cs);
-    });
-    if (e != hipSuccess) return e;
-    if (scores_out) {
-      e = timed(4, cs, [&] {
-        return kpool::launch_scores_copy(ws, ld, c1 - c0, cu_seqlens_dev, nseq, c0, kpool,
-                                         scores_out + (c0 - q_lo) * max_pools, max_pools, cs);
-      });
-    }
-    return e;
-  };
-
-  if (nbuf == 1 || nchunks == 1) {
-    for (int64_t c0 = q_lo; c0 < q_hi; c0 += chunk_rows) {
-      hipError_t e = enqueue_chunk(c0, std::min(q_hi, c0 + chunk_rows), ws_buf[0], gws_buf[0], st);
-      if (e != hipSuccess) return hip_fail(fn, e);
-    }
-    return ok();
-  }
-  // chunk c goes to buffer c % 2 on stream c % 2; chunk c + 2 reuses the buffer after
-  // chunk c's selection because both sit on the same stream
-  Aux *aux = nullptr;
-  hipError_t e = get_aux(st, &aux);
-  if (e != hipSuccess) return hip_fail(fn, e);
-  std::lock_guard<std::mutex> guard(aux->mu);
-  hipStream_t streams[2] = {st, aux->helper};
-  e = hipEventRecord(aux->fork, st);
-  if (e == hipSuccess) e = hipStreamWaitEvent(aux->helper, aux->fork, 0);
-  if (e != hipSuccess) return hip_fail(fn, e);
-  hipError_t first_err = hipSuccess;
-  int64_t c = 0;
-  for (int64_t c0 = q_lo; c0 < q_hi && first_err == hipSuccess; c0 += chunk_rows, ++c)
-    first_err = enqueue_chunk(c0, std::min(q_hi, c0 + chunk_rows), ws_buf[c & 1], gws_buf[c & 1],
-                              streams[c & 1]);
-  // join: the caller's stream waits for the helper whatever happened above
-  e = hipEventRecord(aux->join, aux->helper);
-  if (e == hipSuccess) e = hipStreamWaitEvent(st, aux->join, 0);
-  if (first_err != hipSuccess) return hip_fail(fn, first_err);
-  if (e != hipSuccess) return hip_fail(fn, e);
-  return ok();
+int kpool_score_topk_noalloc(const uint16_t *q, const uint16_t *kp, const float *w,
+                             const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                             int32_t nseq, int32_t H, int32_t D, int32_t kpool, float scale,
+                             int64_t q_lo, int64_t q_hi, int32_t budget, int32_t *pool_ids,
+                             float *scores_out, void *stream) {
+  return score_topk_impl("kpool_score_topk_noalloc", q, kp, w, cu_seqlens_host, cu_seqlens_dev, nseq,
+                         H, D, kpool, scale, q_lo, q_hi, budget, nullptr, 0, 0, true, pool_ids,
+                         scores_out, stream);
 }
 
 int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,

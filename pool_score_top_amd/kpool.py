@@ -46,6 +46,8 @@ def lib():
         "kpool_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "kpool_score_topk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i64, i64,
                                             i32, vp, sz, ctypes.c_uint32, vp, vp, vp]),
+        "kpool_score_topk_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                                    i64, i64, i32, vp, vp, vp]),
         "kpool_expand": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, i64, i32, vp, vp]),
         "kpool_topk": (ctypes.c_int, [vp, i64, vp, i64, i32, vp, vp]),
         "kpool_profile_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -180,6 +182,26 @@ def score_topk(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_
                                 KPOOL_FLAG_OVERLAP if overlap else 0, _p(pool_ids),
                                 _p(scores_out), _stream(stream))
     _check(rc, "kpool_score_topk")
+    return pool_ids, scores_out
+
+
+def score_topk_noalloc(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int,
+                       q_lo: int, q_hi: int, pool_ids, scores_out=None, scale: float | None = None,
+                       stream=None):
+    """score_topk through the library's static scratch (kpool_score_topk_noalloc): the
+    caller passes every output; nothing is allocated here or in the library."""
+    import torch
+    _need(q, "q", 2)
+    _need(kp, "kp", 2)
+    _need(w, "w", dtype=torch.float32)
+    cu, cup = _host_i32(cu_seqlens)
+    H, D = q.shape[-2], q.shape[-1]
+    if scale is None:
+        scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    rc = lib().kpool_score_topk_noalloc(_p(q), _p(kp), _p(w), cup, _p(cu_seqlens_dev), len(cu) - 1,
+                                        H, D, kpool, ctypes.c_float(scale), q_lo, q_hi, budget,
+                                        _p(pool_ids), _p(scores_out), _stream(stream))
+    _check(rc, "kpool_score_topk_noalloc")
     return pool_ids, scores_out
 
 
