@@ -7,8 +7,10 @@ and has no CPU fallback.
 from .kpool_oracle import (  # noqa: F401
     bf16_to_f32,
     f32_to_bf16_rne,
+    f64_to_bf16_rne,
     count_pools,
     pool_keys,
+    pool_keys_gated,
     row_positions,
     visible_pools,
     row_scores,

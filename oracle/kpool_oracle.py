@@ -15,6 +15,10 @@ Steps, in the order the pages describe the selection op:
   O1  pool_keys     each pool's key = mean of its kpool consecutive keys
                     (fp32 sum in token order starting from +0, fp32 divide,
                     bf16 round-to-nearest-even)
+  O1g pool_keys_gated  the gated alternative: per dim, a softmax over the
+                    pool's slots of (gate score + slot embedding) weights the
+                    keys (fp64, one bf16 rounding).  The formula is a reading:
+                    parity against the pages' own operator is unpinned
   O2  row_scores    fp64  S[i,p] = sum_h w[i,h] * relu(scale * <q[i,h], kp[p]>)
                     over the pools visible to row i (p*kpool <= t)
   O3  select_row    order the visible pools by (score desc, pool index asc),
@@ -48,8 +52,10 @@ import numpy as np
 __all__ = [
     "bf16_to_f32",
     "f32_to_bf16_rne",
+    "f64_to_bf16_rne",
     "count_pools",
     "pool_keys",
+    "pool_keys_gated",
     "row_positions",
     "visible_pools",
     "row_scores",
@@ -143,6 +149,70 @@ def pool_keys(k_bits, cu_seqlens, kpool: int) -> np.ndarray:
             mean = (acc / np.float32(rem)).astype(np.float32)
             out[base + nfull] = f32_to_bf16_rne(mean)
     return out
+
+
+def f64_to_bf16_rne(x) -> np.ndarray:
+    """fp64 -> bf16 bits, one round to nearest (ties to even) from the fp64 value.
+
+    x = m * 2**e with 0.5 <= |m| < 1 (frexp); a bf16 number has 8 significant
+    bits, so the result is rint(m * 2**8) * 2**(e - 8) (rint rounds half to
+    even), with the quantum held at 2**-133 below the smallest normal bf16
+    exponent (subnormals) and overflow past the largest bf16 going to inf.
+    The value is exact in fp32, whose upper 16 bits are then the bf16 pattern.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    e = np.maximum(e, -125)                     # 2**(e-1) >= 2**-126: fixed quantum below
+    q = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+    q = np.where(np.abs(q) >= 2.0 ** 128, np.copysign(np.inf, x), q)
+    q = np.where(np.isfinite(x), q, x)
+    with np.errstate(over="ignore"):
+        f = q.astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def pool_keys_gated(k_bits, g_bits, ape, cu_seqlens, kpool: int, return_values: bool = False):
+    """Gated pooled keys, bf16 bits ``[P_tot, D]`` (and their fp64 values if asked).
+
+    PARITY UNPINNED AGAINST THE PAGES: they name the GLM-5.3 indexer's k-pool
+    compression tensors -- a gate projection [index_head_dim, hidden] and an
+    absolute position embedding [index_kpool, index_head_dim] (Atlas inference
+    docs, glm5next_dsa/tp.rs, the indexer tensors of the shard plan) -- and say
+    the op takes gate scores as an input (Megatron-LM PR #8299, "Mechanism"),
+    but give no formula.  This is the reading adopted (the pins in
+    tests/test_oracle_gated.py fix this reading, not the pages' operator):
+
+      for pool p of sequence s, tokens t_j = start_s + p*kpool + j, j < n_p,
+      and every dim d:
+        z_j   = g[t_j, d] + ape[j, d]                       (gate score + slot embedding)
+        a_j   = exp(z_j - max_j z_j) / sum_j exp(z_j - max_j z_j)   (softmax over the slots)
+        kp[p, d] = bf16_rne( sum_j a_j * k[t_j, d] )
+
+    A trailing partial pool (n_p < kpool) uses the slot embeddings of the slots
+    it has, ape[0 .. n_p - 1].  Arithmetic in fp64 from the bf16 keys and gate
+    scores (g = the gate projection's output, one value per token and dim) and
+    the fp32 embeddings, rounded once to bf16.
+    """
+    k = bf16_to_f32(k_bits).astype(np.float64)
+    g = bf16_to_f32(g_bits).astype(np.float64)
+    a = np.asarray(ape, dtype=np.float32).astype(np.float64)
+    if k.ndim != 2 or g.shape != k.shape or a.shape != (kpool, k.shape[1]):
+        raise ValueError("need k, g [T, D] and ape [kpool, D]")
+    D = k.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cu_pools, _ = count_pools(cu, kpool)
+    vals = np.zeros((int(cu_pools[-1]), D), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        start, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        for p in range((L + kpool - 1) // kpool):
+            t0 = start + p * kpool
+            n = min(kpool, L - p * kpool)
+            z = g[t0:t0 + n] + a[:n]                   # [n, D]
+            e = np.exp(z - z.max(axis=0))              # softmax over the n slots, per dim
+            wts = e / e.sum(axis=0)
+            vals[int(cu_pools[s]) + p] = (wts * k[t0:t0 + n]).sum(axis=0)
+    bits = f64_to_bf16_rne(vals)
+    return (bits, vals) if return_values else bits
 
 
 # ---------------------------------------------------------------------------

@@ -21,6 +21,8 @@ tokens; head dim 128):
   sq524288   one sequence of 524288 tokens (and its last 1/8 row slice)
   *_k1       the same shapes with kpool 1 (the per-token indexer: every token is a
              pool) and budget 2048 = index_topk
+  *_gated    the same shapes with gate scores g [T, D] (N(0,1) rounded to bf16)
+             and slot embeddings ape [kpool, D] (fp32 N(0,1)) for the gated pooling
 
 q and k are N(0,1) draws rounded to bf16; w is fp32.
 """
@@ -35,7 +37,7 @@ import numpy as np
 BLOCK_ROWS = 4096
 
 # tensor ids for the seed sequence
-_Q, _K, _W, _CU = 1, 2, 3, 4
+_Q, _K, _W, _CU, _G, _APE = 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)
@@ -54,6 +56,8 @@ class Workload:
     q_hi: int | None = None
     # test-only variants: "w_zero", "w_neg", "k_ternary", "k_const"
     variant: str = ""
+    # "mean" pooling, or "gated" (gate scores g [T, D] and slot embeddings ape [kpool, D])
+    pooling: str = "mean"
     extra: dict = field(default_factory=dict)
 
     @property
@@ -74,6 +78,12 @@ WORKLOADS = {
     "thd65536_k1": Workload("thd65536_k1", 65536, 32, 128, 1, 2048, 32.0, layout="thd"),
     "sq262144_k1": Workload("sq262144_k1", 262144, 32, 128, 1, 2048, 32.0),
     "sq524288_k1": Workload("sq524288_k1", 524288, 32, 128, 1, 2048, 32.0),
+    # gated k-pool compression: the same shapes with gate scores and slot embeddings
+    "tiny_gated": Workload("tiny_gated", 64, 4, 16, 4, 4, 1.0, pooling="gated"),
+    "sq4096_gated": Workload("sq4096_gated", 4096, 32, 128, 4, 512, 32.0, pooling="gated"),
+    "thd65536_gated": Workload("thd65536_gated", 65536, 32, 128, 4, 512, 32.0, layout="thd",
+                               pooling="gated"),
+    "sq524288_gated": Workload("sq524288_gated", 524288, 32, 128, 4, 512, 32.0, pooling="gated"),
 }
 
 
@@ -146,13 +156,25 @@ def w_block(wl: Workload, seed: int, block: int) -> np.ndarray:
     return (u / np.float32(wl.w_div)).astype(np.float32)
 
 
+def g_block(wl: Workload, seed: int, block: int) -> np.ndarray:
+    """Gate scores (the gate projection's output), N(0,1) rounded to bf16, [rows, D]."""
+    rows = _block_rows(wl, block)
+    x = _rng(seed, _G, block).standard_normal((rows, wl.D), dtype=np.float32)
+    return _to_bf16_bits(x)
+
+
+def ape(wl: Workload, seed: int) -> np.ndarray:
+    """Slot embeddings of the gated pooling, fp32 N(0,1), [kpool, D]."""
+    return _rng(seed, _APE, 0).standard_normal((wl.kpool, wl.D), dtype=np.float32)
+
+
 def _blocks(lo: int, hi: int):
     return range(lo // BLOCK_ROWS, (hi + BLOCK_ROWS - 1) // BLOCK_ROWS)
 
 
 def rows(wl: Workload, seed: int, lo: int, hi: int, which=("q", "k", "w")):
     """Regenerate rows [lo, hi) of q, k and/or w (host numpy arrays)."""
-    gens = {"q": q_block, "k": k_block, "w": w_block}
+    gens = {"q": q_block, "k": k_block, "w": w_block, "g": g_block}
     out = {}
     for name in which:
         parts = []
@@ -167,8 +189,11 @@ def rows(wl: Workload, seed: int, lo: int, hi: int, which=("q", "k", "w")):
 
 def host_inputs(wl: Workload, seed: int = 0) -> dict:
     """Whole workload on the host (small workloads only)."""
-    r = rows(wl, seed, 0, wl.T)
+    gated = wl.pooling == "gated"
+    r = rows(wl, seed, 0, wl.T, ("q", "k", "w", "g") if gated else ("q", "k", "w"))
     r["cu_seqlens"] = cu_seqlens(wl, seed)
+    if gated:
+        r["ape"] = ape(wl, seed)
     return r
 
 
@@ -186,15 +211,25 @@ def device_inputs(wl: Workload, seed: int = 0, device="cuda", threads: int | Non
     w = torch.empty((wl.T, wl.H), dtype=torch.float32, device=device)
     nblk = (wl.T + BLOCK_ROWS - 1) // BLOCK_ROWS
 
+    gated = wl.pooling == "gated"
+    g = torch.empty((wl.T, wl.D), dtype=torch.int16, device=device) if gated else None
+
     def make(b):
-        return b, q_block(wl, seed, b), k_block(wl, seed, b), w_block(wl, seed, b)
+        return (b, q_block(wl, seed, b), k_block(wl, seed, b), w_block(wl, seed, b),
+                g_block(wl, seed, b) if gated else None)
 
     with ThreadPoolExecutor(threads) as ex:
-        for b, qb, kb, wb in ex.map(make, range(nblk)):
+        for b, qb, kb, wb, gb in ex.map(make, range(nblk)):
             lo = b * BLOCK_ROWS
             hi = lo + len(qb)
             q[lo:hi].copy_(torch.from_numpy(qb.view(np.int16)))
             k[lo:hi].copy_(torch.from_numpy(kb.view(np.int16)))
             w[lo:hi].copy_(torch.from_numpy(wb))
+            if gated:
+                g[lo:hi].copy_(torch.from_numpy(gb.view(np.int16)))
     cu = cu_seqlens(wl, seed)
-    return {"q": q, "k": k, "w": w, "cu_seqlens": cu}
+    out = {"q": q, "k": k, "w": w, "cu_seqlens": cu}
+    if gated:
+        out["g"] = g
+        out["ape"] = torch.from_numpy(ape(wl, seed)).to(device)
+    return out

@@ -200,3 +200,91 @@ def test_mutant_is_caught(name, monkeypatch):
     except (ValueError, IndexError):
         ok = False
     assert not ok, f"mutant {name} survived the pins"
+
+
+# --------------------------- gated pooling ---------------------------------
+
+def _gated_battery():
+    """True iff every pin of tests/test_oracle_gated.py holds for the bound oracle."""
+    import test_oracle_gated as tg
+    checks = [lambda c=c: tg.test_gated_hand_values(c) for c in tg.gated_cases()]
+    checks += [lambda k=k: tg.test_equal_gates_give_the_exact_mean(k) for k in (1, 2, 3, 4, 5)]
+    checks += [tg.test_common_shift_per_dim_changes_nothing, tg.test_dominant_slot_returns_that_key,
+               tg.test_kpool_one_returns_the_keys]
+    checks += [lambda k=k, s=s: tg.test_matches_high_precision_evaluation(k, s)
+               for k, s in ((2, 0), (3, 1), (4, 2), (5, 3))]
+    for c in checks:
+        try:
+            with np.errstate(all="ignore"):
+                c()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            return False
+    return True
+
+
+def _gated_variant(axis_d=False, no_shift=False, ape_rev=False, ape_right=False, no_norm=False,
+                   no_gate=False, no_ape=False, f32=False, via_f32=False, wrong_token=False,
+                   softmin=False):
+    def pool_keys_gated(k_bits, g_bits, ape, cu_seqlens, kpool, return_values=False):
+        dt = np.float32 if f32 else np.float64
+        k = ko.bf16_to_f32(k_bits).astype(dt)
+        g = ko.bf16_to_f32(g_bits).astype(dt)
+        a = np.asarray(ape, np.float32).astype(dt)
+        D = k.shape[1]
+        cu = np.asarray(cu_seqlens, np.int64)
+        cu_pools, _ = ko.count_pools(cu, kpool)
+        vals = np.zeros((int(cu_pools[-1]), D), dt)
+        for s in range(len(cu) - 1):
+            start, L = int(cu[s]), int(cu[s + 1] - cu[s])
+            for p in range((L + kpool - 1) // kpool):
+                t0 = start + p * kpool
+                n = min(kpool, L - p * kpool)
+                slots = np.arange(n)
+                if ape_rev:
+                    slots = kpool - 1 - slots
+                if ape_right:
+                    slots = kpool - n + slots
+                z = (0 if no_gate else g[t0:t0 + n]) + (0 if no_ape else a[slots])
+                z = np.broadcast_to(z, (n, D)).astype(dt)
+                if softmin:
+                    z = -z
+                ax = 1 if axis_d else 0
+                e = np.exp(z) if no_shift else np.exp(z - z.max(axis=ax, keepdims=True))
+                wts = e if no_norm else e / e.sum(axis=ax, keepdims=True)
+                kk = k[t0:t0 + n]
+                if wrong_token:
+                    kk = np.roll(kk, 1, axis=0)
+                vals[int(cu_pools[s]) + p] = (wts * kk).sum(axis=0)
+        if via_f32:
+            bits = ko.f32_to_bf16_rne(vals.astype(np.float32))
+        else:
+            bits = ko.f64_to_bf16_rne(vals.astype(np.float64))
+        return (bits, vals.astype(np.float64)) if return_values else bits
+    return pool_keys_gated
+
+
+GATED_MUTANTS = {
+    "gated_softmax_over_dims": _gated_variant(axis_d=True),
+    "gated_no_max_shift": _gated_variant(no_shift=True),
+    "gated_embedding_slots_reversed": _gated_variant(ape_rev=True),
+    "gated_embedding_right_aligned": _gated_variant(ape_right=True),
+    "gated_not_normalised": _gated_variant(no_norm=True),
+    "gated_gate_dropped": _gated_variant(no_gate=True),
+    "gated_embedding_dropped": _gated_variant(no_ape=True),
+    "gated_fp32_arithmetic": _gated_variant(f32=True),
+    "gated_rounded_through_fp32": _gated_variant(via_f32=True),
+    "gated_weights_on_wrong_token": _gated_variant(wrong_token=True),
+    "gated_softmin": _gated_variant(softmin=True),
+}
+
+
+def test_unmodified_gated_oracle_passes_battery():
+    assert _gated_battery()
+
+
+@pytest.mark.parametrize("name", sorted(GATED_MUTANTS))
+def test_gated_mutant_is_caught(name, monkeypatch):
+    import oracle
+    monkeypatch.setattr(ko, "pool_keys_gated", GATED_MUTANTS[name])
+    monkeypatch.setattr(oracle, "pool_keys_gated", GATED_MUTANTS[name])
+    assert not _gated_battery(), f"mutant {name} survived the pins"
