@@ -82,8 +82,14 @@ def cpu_baseline(wl, inp, total_pairs, seed, budget_s=15.0):
     cu = np.asarray(inp["cu_seqlens"])
     lo, hi = wl.rows
     k = inp["k"].cpu().numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    kp = oracle.pool_keys(k, cu, wl.kpool)
+    if wl.pooling == "gated":
+        g = inp["g"].cpu().numpy().view(np.uint16)
+        ape = inp["ape"].cpu().numpy()
+        t0 = time.perf_counter()
+        kp = oracle.pool_keys_gated(k, g, ape, cu, wl.kpool)
+    else:
+        t0 = time.perf_counter()
+        kp = oracle.pool_keys(k, cu, wl.kpool)
     t_pool = time.perf_counter() - t0
     cu_pools, _ = oracle.count_pools(cu, wl.kpool)
     # 64 evenly spaced rows (always the first and last), then random rows until the time budget
@@ -262,7 +268,7 @@ def main():
     flops = 2.0 * wl.H * wl.D * pairs
 
     for i in range(args.warmup):
-        sel.run(inp["q"], inp["k"], inp["w"])
+        sel.run(inp["q"], inp["k"], inp["w"], g=inp.get("g"), ape=inp.get("ape"))
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i} done")
 
@@ -274,7 +280,7 @@ def main():
     t0 = time.perf_counter()
     step_ev[0].record()
     for i in range(args.steps):
-        sel.run(inp["q"], inp["k"], inp["w"])
+        sel.run(inp["q"], inp["k"], inp["w"], g=inp.get("g"), ape=inp.get("ape"))
         step_ev[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -289,7 +295,7 @@ def main():
     torch.cuda.synchronize()
     tk = time.perf_counter()
     for i in range(args.steps):
-        sel.run(inp["q"], inp["k"], inp["w"], overlap=False)
+        sel.run(inp["q"], inp["k"], inp["w"], overlap=False, g=inp.get("g"), ape=inp.get("ape"))
     torch.cuda.synchronize()
     ms_serial = 1000.0 * (time.perf_counter() - tk) / args.steps
     prof = K.profile_collect()
@@ -307,7 +313,8 @@ def main():
     topk_gbs = topk_bytes * S / (topk_ms / 1000.0) / 1e9
     exp_bytes = 4.0 * wl.budget * rows * (1 + wl.kpool)
     exp_gbs = exp_bytes * S / (exp_ms / 1000.0) / 1e9 if exp_ms > 0 else 0.0
-    pool_bytes = 2.0 * wl.T * wl.D + 2.0 * sel.P_tot * wl.D
+    # keys (and, for the gated pooling, gate scores) read once, pooled keys written once
+    pool_bytes = (4.0 if wl.pooling == "gated" else 2.0) * wl.T * wl.D + 2.0 * sel.P_tot * wl.D
     pool_gbs = pool_bytes * S / (pool_ms / 1000.0) / 1e9 if pool_ms > 0 else 0.0
 
     cnt = committed_counters(wl.name)
@@ -355,9 +362,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{wl.name}: {len(cu) - 1} sequence(s), {wl.T} tokens, rows [{q_lo}, {q_hi}), "
-                         f"H={wl.H}, D={wl.D}, kpool={wl.kpool}, budget={wl.budget} pools, causal"),
+                         f"H={wl.H}, D={wl.D}, kpool={wl.kpool}, budget={wl.budget} pools, causal, "
+                         f"{wl.pooling} pooling"),
             "tokens": wl.T, "rows": rows, "H": wl.H, "D": wl.D, "kpool": wl.kpool,
-            "budget": wl.budget, "visible_pairs": pairs, "seed": args.seed,
+            "budget": wl.budget, "visible_pairs": pairs, "seed": args.seed, "pooling": wl.pooling,
             "score_chunk_rows": chunk_rows,
             "chunk_overlap": args.overlap,
             "workspace_bytes": sel.workspace_bytes,

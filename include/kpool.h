@@ -85,6 +85,27 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host,
                     const int32_t *cu_seqlens_dev, const int32_t *cu_pools_dev,
                     int32_t nseq, int32_t D, int32_t kpool, uint16_t *kp, void *stream);
 
+/* Step 1, gated variant - the GLM-5.3 indexer's k-pool compression (Atlas inference
+ * docs, glm5next_dsa/tp.rs: the shard plan's indexer tensors include a compression
+ * gate [index_head_dim, hidden] and a slot embedding [index_kpool, index_head_dim];
+ * Megatron-LM PR #8299 "Mechanism": gate scores are an input of the op).  The pages
+ * give no formula; this library's reading, for pool p of sequence s with tokens
+ * t_j = cu_seqlens[s] + p*kpool + j, j < n = min(kpool, L_s - p*kpool), and each dim d:
+ *   z_j = g[t_j, d] + ape[j, d],  m = max_j z_j,  e_j = exp(z_j - m)
+ *   kp[cu_pools[s] + p, d] = bf16_rne( (sum_j e_j * k[t_j, d]) / (sum_j e_j) )
+ * in fp64, rounded once to bf16 (sums in slot order; a trailing partial pool uses
+ * ape[0 .. n-1]).
+ *   k    bf16 [T, D]      keys
+ *   g    bf16 [T, D]      gate scores (the gate projection's output per token and dim)
+ *   ape  fp32 [kpool, D]  slot embeddings
+ *   kp   bf16 [P_tot, D]  output, laid out as for kpool_pool_keys
+ * k, g, ape and kp must be 16-byte aligned; D a multiple of 8 (<= 1024); kpool >= 1.
+ * Inputs must be finite. */
+int kpool_pool_keys_gated(const uint16_t *k, const uint16_t *g, const float *ape,
+                          const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                          const int32_t *cu_pools_dev, int32_t nseq, int32_t D, int32_t kpool,
+                          uint16_t *kp, void *stream);
+
 /* Workspace for kpool_score_topk over rows [q_lo, q_hi): per query row of a
  * chunk, one fp32 score row at a pitch of max_pools rounded up to 64 plus one
  * fp32 maximum per 16 pools of it; the score rows of one chunk are capped at

@@ -404,6 +404,30 @@ int kpool_score_topk_noalloc(const uint16_t *q, const uint16_t *kp, const float 
                          scores_out, stream);
 }
 
+int kpool_pool_keys_gated(const uint16_t *k, const uint16_t *g, const float *ape,
+                          const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
+                          const int32_t *cu_pools_dev, int32_t nseq, int32_t D, int32_t kpool,
+                          uint16_t *kp, void *stream) {
+  const char *fn = "kpool_pool_keys_gated";
+  int rc = check_cu(cu_seqlens_host, nseq, fn);
+  if (rc) return rc;
+  if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
+  if (D < 8 || D > 1024 || D % 8) return fail(KPOOL_EINVAL, "%s: D must be a multiple of 8 in [8, 1024] (got %d)", fn, D);
+  const int64_t P_tot = kpool_count_pools(cu_seqlens_host, nseq, kpool, nullptr, nullptr);
+  if (P_tot < 0) return (int)P_tot;
+  if (P_tot == 0) return ok();
+  if (!k || !g || !ape || !kp || !cu_seqlens_dev || !cu_pools_dev) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
+  if (!aligned16(k) || !aligned16(g) || !aligned16(ape) || !aligned16(kp))
+    return fail(KPOOL_EINVAL, "%s: k, g, ape and kp must be 16-byte aligned", fn);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(0, st, [&] {
+    return kpool::launch_pool_keys_gated(k, g, ape, cu_seqlens_dev, cu_pools_dev, nseq, D, kpool,
+                                         P_tot, kp, st);
+  });
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return ok();
+}
+
 int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                  int32_t nseq, int32_t kpool, int64_t q_lo, int64_t q_hi, int32_t budget,
                  int32_t *token_ids, void *stream) {

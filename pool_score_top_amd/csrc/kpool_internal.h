@@ -32,6 +32,11 @@ hipError_t launch_pool_keys(const uint16_t *k, const int32_t *cu_seqlens, const 
                             int32_t nseq, int32_t D, int32_t kpool, int64_t P_tot, uint16_t *kp,
                             hipStream_t stream);
 
+hipError_t launch_pool_keys_gated(const uint16_t *k, const uint16_t *g, const float *ape,
+                                  const int32_t *cu_seqlens, const int32_t *cu_pools, int32_t nseq,
+                                  int32_t D, int32_t kpool, int64_t P_tot, uint16_t *kp,
+                                  hipStream_t stream);
+
 // true if (H, D) has a compiled score kernel
 bool score_supported(int H, int D);
 int score_tile_rows();

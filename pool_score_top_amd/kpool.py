@@ -43,6 +43,7 @@ def lib():
         "kpool_version": (ctypes.c_int, []),
         "kpool_count_pools": (i64, [vp, i32, i32, vp, vp]),
         "kpool_pool_keys": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "kpool_pool_keys_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]),
         "kpool_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "kpool_score_topk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i64, i64,
                                             i32, vp, sz, ctypes.c_uint32, vp, vp, vp]),
@@ -143,6 +144,28 @@ def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None,
     rc = lib().kpool_pool_keys(_p(k), cup, _p(cu_seqlens_dev), _p(cu_pools_dev), nseq, D, kpool,
                                _p(out), _stream(stream))
     _check(rc, "kpool_pool_keys")
+    return out
+
+
+def pool_keys_gated(k, g, ape, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None,
+                    stream=None):
+    """Gated pooled keys: k, g bf16 [T, D] (int16 storage), ape fp32 [kpool, D]."""
+    import torch
+    _need(k, "k", 2)
+    _need(g, "g", 2)
+    _need(ape, "ape", dtype=torch.float32)
+    cu, cup = _host_i32(cu_seqlens)
+    nseq = len(cu) - 1
+    _, _, P_tot = count_pools(cu, kpool)
+    D = k.shape[-1]
+    if tuple(g.shape) != tuple(k.shape) or tuple(ape.shape) != (kpool, D):
+        raise ValueError("need g shaped like k and ape [kpool, D]")
+    if out is None:
+        with _on(stream):
+            out = torch.empty((P_tot, D), dtype=k.dtype, device=k.device)
+    rc = lib().kpool_pool_keys_gated(_p(k), _p(g), _p(ape), cup, _p(cu_seqlens_dev), _p(cu_pools_dev),
+                                     nseq, D, kpool, _p(out), _stream(stream))
+    _check(rc, "kpool_pool_keys_gated")
     return out
 
 
@@ -296,9 +319,17 @@ class Selector:
         nbuf = 2 if overlap and self.workspace_bytes >= 2 * row_bytes else 1
         return max(1, min((1 << 31) // (ld * 4), self.workspace_bytes // nbuf // row_bytes))
 
-    def run(self, q, k, w, scores_out=None, stream=None, overlap: bool | None = None):
+    def run(self, q, k, w, scores_out=None, stream=None, overlap: bool | None = None, g=None,
+            ape=None):
+        """One pass of the path; with gate scores g and slot embeddings ape the keys are
+        pooled by the gated compression, otherwise by the mean."""
         overlap = self.overlap if overlap is None else overlap
-        pool_keys(k, self.cu, self.cu_dev, self.cu_pools_dev, self.kpool, out=self.kp, stream=stream)
+        if g is not None:
+            pool_keys_gated(k, g, ape, self.cu, self.cu_dev, self.cu_pools_dev, self.kpool,
+                            out=self.kp, stream=stream)
+        else:
+            pool_keys(k, self.cu, self.cu_dev, self.cu_pools_dev, self.kpool, out=self.kp,
+                      stream=stream)
         score_topk(q, self.kp, w, self.cu, self.cu_dev, self.kpool, self.budget, self.q_lo, self.q_hi,
                    scale=self.scale, workspace=self.workspace, pool_ids=self.pool_ids,
                    scores_out=scores_out, overlap=overlap, stream=stream)

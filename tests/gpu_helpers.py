@@ -219,3 +219,58 @@ def oracle_rows(inputs, kpool, rows, kp=None, width=None):
     s = oracle.row_scores(inputs["q"][rows], inputs["w"][rows], kp, cu_pools, seq, t, kpool,
                           width=max_pools if width is None else width)
     return kp, s, t
+
+
+def gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool, u=2.0 ** -53):
+    """Bounds [lo, hi] (fp32 values of bf16 numbers) that the GPU's gated pooled keys may take.
+
+    vals: the oracle's fp64 values of the gated pooled keys.  The GPU evaluates the
+    same reading in floating point with unit roundoff u (fp64 in the kernel; the
+    oracle's own fp64 evaluation errs the same way): z_j = g + ape, z_j - m, e_j = exp
+    (an error of a few ulp), the slot sums and one divide.  First-order error analysis
+    gives |gpu - value| <= delta = 2 (2 (eps_e + n u) + u) A, where
+    eps_e = 4 u max_j |z_j| + 4 u bounds the relative error of each e_j,
+    A = sum_j e_j |k_j| / sum_j e_j, and the factor 2 is a margin; it is doubled once
+    more because the oracle's value carries an error of the same kind.  The GPU's bf16
+    must then lie between the roundings of value - delta and value + delta: the
+    rounding of the value itself, except where the value sits within delta of a
+    rounding midpoint.  Returns (lo, hi, ambiguous mask)."""
+    import oracle as O
+    k = O.bf16_to_f32(k_bits).astype(np.float64)
+    g = O.bf16_to_f32(g_bits).astype(np.float64)
+    a = np.asarray(ape, np.float32).astype(np.float64)
+    cu = np.asarray(cu_seqlens, np.int64)
+    cu_pools, _ = O.count_pools(cu, kpool)
+    delta = np.zeros_like(vals)
+    for s in range(len(cu) - 1):
+        start, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        P = (L + kpool - 1) // kpool
+        for j0 in range(0, P, 4096):                       # pools in blocks, vectorised
+            ps = np.arange(j0, min(P, j0 + 4096))
+            for n in np.unique(np.minimum(kpool, L - ps * kpool)):
+                sel = ps[np.minimum(kpool, L - ps * kpool) == n]
+                t = start + sel[:, None] * kpool + np.arange(n)[None, :]      # [np, n]
+                z = g[t] + a[None, :n]                                        # [np, n, D]
+                m = z.max(axis=1, keepdims=True)
+                e = np.exp(z - m)
+                A = (e * np.abs(k[t])).sum(axis=1) / e.sum(axis=1)
+                eps_e = 4 * u * np.abs(z).max(axis=1) + 4 * u
+                delta[int(cu_pools[s]) + sel] = 4 * (2 * (eps_e + n * u) + u) * A
+    lo = O.bf16_to_f32(O.f64_to_bf16_rne(vals - delta))
+    hi = O.bf16_to_f32(O.f64_to_bf16_rne(vals + delta))
+    return lo, hi, lo != hi
+
+
+def check_gated_keys(gpu_bits, vals, k_bits, g_bits, ape, cu_seqlens, kpool, where=""):
+    """The GPU's gated pooled keys against the oracle's values (rule in gated_allowed)."""
+    import oracle as O
+    lo, hi, amb = gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool)
+    got = O.bf16_to_f32(gpu_bits)
+    bad = (got < lo) | (got > hi)
+    assert not bad.any(), (f"{where}: {bad.sum()} gated keys outside the error bound, first at "
+                           f"{np.argwhere(bad)[0].tolist()}")
+    exact = O.f64_to_bf16_rne(vals)
+    st = {"keys": int(vals.size), "near_midpoint": int(amb.sum()),
+          "differ_from_oracle_bits": int((gpu_bits != exact).sum())}
+    assert st["differ_from_oracle_bits"] <= st["near_midpoint"]
+    return st
