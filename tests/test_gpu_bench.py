@@ -31,6 +31,12 @@ def test_bench_prints_one_complete_json_line():
     assert 0.0 < rl["frac"] < 1.0 and abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-9
     assert r["step_ms"]["min"] <= r["step_ms"]["median"] <= r["step_ms"]["max"]
     assert r["probe_peaks"]["hbm_copy_GBs"] > 0 and r["probe_peaks"]["bf16_gemm_TFLOPs"] > 0
+    c = r["config"]
+    assert c["chunk_buffers"] in (1, 2) and c["workspace_bytes"] > 0 and c["pooling"] == "mean"
+    assert c["score_bytes_in_flight"] == c["chunk_buffers"] * c["score_bytes_per_chunk_buffer"]
+    tk = r["kernels"]["topk"]
+    assert tk["frac"] is None or 0.0 < tk["frac"] <= 1.0       # counter bytes, never above the peak
+    assert tk["frac_if_every_score_were_read"] > 0
 
 
 def test_bench_refuses_more_than_one_gpu():
