@@ -24,7 +24,11 @@ Steps, in the order the pages describe the selection op:
   O3  select_row    order the visible pools by (score desc, pool index asc),
                     keep the first `budget`, pad with -1
   O4  expand_row    pool p -> tokens p*kpool + j, -1 where the token lies after
-                    the row (token > t) or the slot is padding
+                    the row (token > t) or the slot is padding; in tail mode
+                    (full pools only) the sequence's trailing L mod kpool tokens
+                    are appended and filtered the same way.  "Tail append" is
+                    named but not defined on the pages: this reading's parity
+                    against the pages' own operator is unpinned
 
 Sources (the pages this build works from):
   * Atlas inference docs, ``spark_model/layers/glm5next_dsa/tp.rs``, module
@@ -98,21 +102,25 @@ def f32_to_bf16_rne(x) -> np.ndarray:
 # O1: pooled keys
 # ---------------------------------------------------------------------------
 
-def count_pools(cu_seqlens, kpool: int):
-    """Pools per sequence = ceil(L_s / kpool); returns (cu_pools, max_pools).
+def count_pools(cu_seqlens, kpool: int, tail: bool = False):
+    """Pools per sequence; returns (cu_pools, max_pools).
 
-    Atlas tp.rs module doc: the pool count is the sequence length over kpool;
-    a trailing partial pool (L_s not a multiple of kpool) is kept (reading).
+    Default: ceil(L_s / kpool), a trailing partial pool (L_s not a multiple of
+    kpool) kept as a pool of its own (reading).  tail=True: the full pools only,
+    floor(L_s / kpool) -- the pool count of Atlas tp.rs module doc,
+    ``n_pools = seq / kpool`` -- and the L_s mod kpool trailing tokens form the
+    sequence's tail, which expand_row appends (reading of Megatron-LM PR #8299
+    "Change": pool expansion, tail append, mask filtering).
     """
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     lens = np.diff(cu)
-    npools = (lens + kpool - 1) // kpool
+    npools = lens // kpool if tail else (lens + kpool - 1) // kpool
     cu_pools = np.concatenate([[0], np.cumsum(npools)]).astype(np.int64)
     max_pools = int(npools.max()) if len(npools) else 0
     return cu_pools, max_pools
 
 
-def pool_keys(k_bits, cu_seqlens, kpool: int) -> np.ndarray:
+def pool_keys(k_bits, cu_seqlens, kpool: int, tail: bool = False) -> np.ndarray:
     """Pooled keys, bf16 bits ``[P_tot, D]``; pools of sequence s start at cu_pools[s].
 
     For pool p of sequence s with n_p = min(kpool, L_s - p*kpool) tokens:
@@ -120,14 +128,15 @@ def pool_keys(k_bits, cu_seqlens, kpool: int) -> np.ndarray:
         kp  = bf16_rne(fp32(acc / n_p)).
     Megatron-LM PR #8299 "Mechanism" (rows score the pooled keys); Atlas
     tp.rs module doc (pools of kpool consecutive tokens).  Mean with fp32
-    accumulation and a bf16 result is the reading this build adopts.
+    accumulation and a bf16 result is the reading this build adopts.  With
+    tail=True only the full pools exist (count_pools).
     """
     k = bf16_to_f32(k_bits)
     if k.ndim != 2:
         raise ValueError("k must be [T, D]")
     D = k.shape[1]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
-    cu_pools, _ = count_pools(cu, kpool)
+    cu_pools, _ = count_pools(cu, kpool, tail)
     out = np.zeros((int(cu_pools[-1]), D), dtype=np.uint16)
     for s in range(len(cu) - 1):
         start, end = int(cu[s]), int(cu[s + 1])
@@ -142,7 +151,7 @@ def pool_keys(k_bits, cu_seqlens, kpool: int) -> np.ndarray:
             mean = (acc / np.float32(kpool)).astype(np.float32)
             out[base:base + nfull] = f32_to_bf16_rne(mean)
         rem = L - nfull * kpool
-        if rem:
+        if rem and not tail:
             acc = np.zeros(D, dtype=np.float32)
             for j in range(rem):
                 acc = (acc + k[start + nfull * kpool + j]).astype(np.float32)
@@ -171,7 +180,8 @@ def f64_to_bf16_rne(x) -> np.ndarray:
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def pool_keys_gated(k_bits, g_bits, ape, cu_seqlens, kpool: int, return_values: bool = False):
+def pool_keys_gated(k_bits, g_bits, ape, cu_seqlens, kpool: int, return_values: bool = False,
+                    tail: bool = False):
     """Gated pooled keys, bf16 bits ``[P_tot, D]`` (and their fp64 values if asked).
 
     PARITY UNPINNED AGAINST THE PAGES: they name the GLM-5.3 indexer's k-pool
@@ -189,7 +199,7 @@ def pool_keys_gated(k_bits, g_bits, ape, cu_seqlens, kpool: int, return_values: 
         kp[p, d] = bf16_rne( sum_j a_j * k[t_j, d] )
 
     A trailing partial pool (n_p < kpool) uses the slot embeddings of the slots
-    it has, ape[0 .. n_p - 1].  Arithmetic in fp64 from the bf16 keys and gate
+    it has, ape[0 .. n_p - 1]; with tail=True only full pools exist.  Arithmetic in fp64 from the bf16 keys and gate
     scores (g = the gate projection's output, one value per token and dim) and
     the fp32 embeddings, rounded once to bf16.
     """
@@ -200,11 +210,11 @@ def pool_keys_gated(k_bits, g_bits, ape, cu_seqlens, kpool: int, return_values: 
         raise ValueError("need k, g [T, D] and ape [kpool, D]")
     D = k.shape[1]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
-    cu_pools, _ = count_pools(cu, kpool)
+    cu_pools, _ = count_pools(cu, kpool, tail)
     vals = np.zeros((int(cu_pools[-1]), D), dtype=np.float64)
     for s in range(len(cu) - 1):
         start, L = int(cu[s]), int(cu[s + 1] - cu[s])
-        for p in range((L + kpool - 1) // kpool):
+        for p in range(int(cu_pools[s + 1] - cu_pools[s])):
             t0 = start + p * kpool
             n = min(kpool, L - p * kpool)
             z = g[t0:t0 + n] + a[:n]                   # [n, D]
@@ -233,9 +243,11 @@ def row_positions(rows, cu_seqlens):
     return s, rows - cu[s]
 
 
-def visible_pools(t, kpool: int):
-    """Number of pools visible to local position t: pools p with p*kpool <= t."""
-    return np.asarray(t, dtype=np.int64) // kpool + 1
+def visible_pools(t, kpool: int, npools=None):
+    """Number of pools visible to local position t: pools p with p*kpool <= t (and,
+    when the sequence has only npools pools, p < npools)."""
+    nv = np.asarray(t, dtype=np.int64) // kpool + 1
+    return nv if npools is None else np.minimum(nv, np.asarray(npools, dtype=np.int64))
 
 
 # ---------------------------------------------------------------------------
@@ -247,7 +259,8 @@ def row_scores(q_rows_bits, w_rows, kp_bits, cu_pools, seq, t, kpool: int,
     """fp64 scores for a set of rows, ``[r, width]``, -inf where a pool is masked.
 
     S[i,p] = sum_h w[i,h] * max(0, scale * sum_d q[i,h,d] * kp[s,p,d])
-    for p < visible_pools(t).  Atlas tp.rs module doc (the head-weighted
+    for p < visible_pools(t) (capped at the sequence's pool count, which
+    cu_pools gives; only tail mode's count can be below it).  Atlas tp.rs module doc (the head-weighted
     ReLU sum); the scale 1/sqrt(D) is this build's reading.  Order of
     operations: dot, times scale, ReLU, times w, sum over heads.
     q_rows_bits: bf16 bits [r, H, D]; w_rows: fp32 [r, H]; kp_bits: [P_tot, D].
@@ -260,7 +273,8 @@ def row_scores(q_rows_bits, w_rows, kp_bits, cu_pools, seq, t, kpool: int,
         scale = 1.0 / np.sqrt(np.float64(D))
     seq = np.asarray(seq, dtype=np.int64)
     t = np.asarray(t, dtype=np.int64)
-    nv = visible_pools(t, kpool)
+    cu_pools = np.asarray(cu_pools, dtype=np.int64)
+    nv = visible_pools(t, kpool, cu_pools[seq + 1] - cu_pools[seq])
     if width is None:
         width = int(nv.max()) if r else 0
     out = np.full((r, width), -np.inf, dtype=np.float64)
@@ -322,16 +336,23 @@ def select_row(scores_row, budget: int) -> np.ndarray:
 # O4: expansion and causal filter
 # ---------------------------------------------------------------------------
 
-def expand_row(ids, t: int, kpool: int) -> np.ndarray:
+def expand_row(ids, t: int, kpool: int, tail=None) -> np.ndarray:
     """Token ids for one row: slot b*kpool+j holds p*kpool+j for p = ids[b].
 
     -1 where the slot is padding (p < 0) or the token comes after the row
     (p*kpool + j > t).  Megatron-LM PR #8299 "Change": pool expansion and
     mask filtering after the pool ids are known; filtered entries stay in
     place as -1 (reading).
+
+    tail = (a, b): tail mode (see count_pools).  The sequence's tail tokens
+    a .. b-1 (sequence-local, b - a < kpool) are appended after the expanded
+    pools in kpool - 1 more slots, and the same causal filter applies to them:
+    slot budget*kpool + j holds a + j if a + j < b and a + j <= t, else -1
+    (the pages' order: expansion, tail append, mask filtering).
     """
     ids = np.asarray(ids, dtype=np.int64)
-    out = np.full(len(ids) * kpool, -1, dtype=np.int32)
+    n_tail = 0 if tail is None else kpool - 1
+    out = np.full(len(ids) * kpool + n_tail, -1, dtype=np.int32)
     for b, p in enumerate(ids):
         if p < 0:
             continue
@@ -339,6 +360,12 @@ def expand_row(ids, t: int, kpool: int) -> np.ndarray:
             tok = p * kpool + j
             if tok <= t:
                 out[b * kpool + j] = tok
+    if tail is not None:
+        a, e = int(tail[0]), int(tail[1])
+        for j in range(n_tail):
+            tok = a + j
+            if tok < e and tok <= t:
+                out[len(ids) * kpool + j] = tok
     return out
 
 
@@ -348,14 +375,16 @@ def expand_row(ids, t: int, kpool: int) -> np.ndarray:
 
 def select(q_bits, k_bits, w, cu_seqlens, kpool: int, budget: int,
            q_lo: int = 0, q_hi: int | None = None, scale: float | None = None,
-           kp_bits=None):
+           kp_bits=None, tail: bool = False):
     """Pool, score, select and expand the rows [q_lo, q_hi) of a packed batch.
 
     Megatron-LM PR #8299 "Change": a query-row range is scored on its own and
     gives, row for row, what the whole range gives.  Returns a dict with
     ``kp`` (bf16 bits), ``scores`` (fp64, -inf where masked, width = the
     largest pool count of any sequence), ``pool_ids`` (int32, [rows, budget])
-    and ``token_ids`` (int32, [rows, budget*kpool]).
+    and ``token_ids`` (int32, [rows, budget*kpool], plus kpool - 1 tail slots
+    in tail mode).  tail=True: full pools only and the tail appended (see
+    count_pools and expand_row).
     """
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     T = int(cu[-1])
@@ -363,13 +392,14 @@ def select(q_bits, k_bits, w, cu_seqlens, kpool: int, budget: int,
         q_hi = T
     if not (0 <= q_lo <= q_hi <= T):
         raise ValueError("bad row range")
-    cu_pools, max_pools = count_pools(cu, kpool)
-    kp = pool_keys(k_bits, cu, kpool) if kp_bits is None else kp_bits
+    cu_pools, max_pools = count_pools(cu, kpool, tail)
+    kp = pool_keys(k_bits, cu, kpool, tail) if kp_bits is None else kp_bits
     rows = np.arange(q_lo, q_hi, dtype=np.int64)
     n = len(rows)
+    n_tail = kpool - 1 if tail else 0
     scores = np.full((n, max_pools), -np.inf, dtype=np.float64)
     pool_ids = np.full((n, budget), -1, dtype=np.int32)
-    token_ids = np.full((n, budget * kpool), -1, dtype=np.int32)
+    token_ids = np.full((n, budget * kpool + n_tail), -1, dtype=np.int32)
     if n:
         seq, t = row_positions(rows, cu)
         q = np.asarray(q_bits)[q_lo:q_hi]
@@ -379,9 +409,13 @@ def select(q_bits, k_bits, w, cu_seqlens, kpool: int, budget: int,
             b = min(n, a + step)
             scores[a:b] = row_scores(q[a:b], ww[a:b], kp, cu_pools, seq[a:b], t[a:b],
                                      kpool, scale, width=max_pools)
-        nv = visible_pools(t, kpool)
+        nv = visible_pools(t, kpool, cu_pools[seq + 1] - cu_pools[seq])
         for i in range(n):
             pool_ids[i] = select_row(scores[i, :nv[i]], budget)
-            token_ids[i] = expand_row(pool_ids[i], int(t[i]), kpool)
+            tl = None
+            if tail:
+                L = int(cu[seq[i] + 1] - cu[seq[i]])
+                tl = (L // kpool * kpool, L)
+            token_ids[i] = expand_row(pool_ids[i], int(t[i]), kpool, tl)
     return {"kp": kp, "scores": scores, "pool_ids": pool_ids, "token_ids": token_ids,
             "cu_pools": cu_pools, "max_pools": max_pools}

@@ -73,14 +73,14 @@ def bf16(x: Fraction) -> Fraction:
     return round_rne(x, BF16_P, BF16_EMIN)
 
 
-def pooled_keys(k_bits, cu_seqlens, kpool):
-    """[P_tot][D] exact values of the stored pooled keys."""
+def pooled_keys(k_bits, cu_seqlens, kpool, tail=False):
+    """[P_tot][D] exact values of the stored pooled keys (tail: full pools only)."""
     out = []
     D = len(k_bits[0])
     for s in range(len(cu_seqlens) - 1):
         start, end = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
         p = 0
-        while p * kpool < end - start:
+        while (p + 1) * kpool <= end - start if tail else p * kpool < end - start:
             toks = range(start + p * kpool, min(end, start + (p + 1) * kpool))
             row = []
             for d in range(D):
@@ -93,8 +93,12 @@ def pooled_keys(k_bits, cu_seqlens, kpool):
     return out
 
 
-def run(q_bits, k_bits, w_f32_bits, cu_seqlens, kpool, budget):
-    """Exact pooled keys, scores, selections and token ids for every row."""
+def run(q_bits, k_bits, w_f32_bits, cu_seqlens, kpool, budget, tail=False):
+    """Exact pooled keys, scores, selections and token ids for every row.
+
+    tail: only the full pools of each sequence are pools, and the sequence's
+    remaining tokens are appended to every row's token list (kpool - 1 slots),
+    causally filtered like the pools' tokens."""
     T = int(cu_seqlens[-1])
     H = len(q_bits[0])
     D = len(q_bits[0][0])
@@ -102,18 +106,19 @@ def run(q_bits, k_bits, w_f32_bits, cu_seqlens, kpool, budget):
     if r * r != D:
         raise ValueError("exact brute force needs a square head dim")
     scale = Fraction(1, r)
-    kp = pooled_keys(k_bits, cu_seqlens, kpool)
-    pool_base = []
+    kp = pooled_keys(k_bits, cu_seqlens, kpool, tail)
+    pool_base, pool_count = [], []
     base = 0
     for s in range(len(cu_seqlens) - 1):
         pool_base.append(base)
         L = int(cu_seqlens[s + 1]) - int(cu_seqlens[s])
-        base += (L + kpool - 1) // kpool
+        pool_count.append(L // kpool if tail else (L + kpool - 1) // kpool)
+        base += pool_count[-1]
     scores, ids, toks = [], [], []
     for i in range(T):
         s = max(j for j in range(len(cu_seqlens) - 1) if int(cu_seqlens[j]) <= i)
         t = i - int(cu_seqlens[s])
-        nvis = t // kpool + 1
+        nvis = len([p for p in range(pool_count[s]) if p * kpool <= t])
         qi = [[decode_bf16(q_bits[i][h][d]) for d in range(D)] for h in range(H)]
         wi = [decode_f32(w_f32_bits[i][h]) for h in range(H)]
         row = []
@@ -130,6 +135,10 @@ def run(q_bits, k_bits, w_f32_bits, cu_seqlens, kpool, budget):
         for p in sel:
             for j in range(kpool):
                 tk.append(p * kpool + j if p >= 0 and p * kpool + j <= t else -1)
+        if tail:
+            L = int(cu_seqlens[s + 1]) - int(cu_seqlens[s])
+            for tok in range(pool_count[s] * kpool, pool_count[s] * kpool + kpool - 1):
+                tk.append(tok if tok < L and tok <= t else -1)
         scores.append(row)
         ids.append(sel)
         toks.append(tk)

@@ -288,3 +288,75 @@ def test_gated_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(ko, "pool_keys_gated", GATED_MUTANTS[name])
     monkeypatch.setattr(oracle, "pool_keys_gated", GATED_MUTANTS[name])
     assert not _gated_battery(), f"mutant {name} survived the pins"
+
+
+# --------------------------- tail mode ---------------------------------------
+
+def _tail_battery():
+    """True iff every pin of tests/test_oracle_tail.py holds for the bound oracle."""
+    import test_oracle_tail as tt
+    checks = [lambda c=c: tt.test_tail_hand_rows(c) for c in tt.tail_cases()]
+    checks += [lambda c=c: tt.test_tail_mode_matches_exact_brute_force(c) for c in tt.BRUTE_CASES]
+    checks += [tt.test_multiple_of_kpool_is_unchanged_by_tail_mode,
+               tt.test_tail_slots_closed_form_and_restriction_to_full_pools]
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            return False
+    return True
+
+
+_orig_expand_row = ko.expand_row
+_orig_count_pools = ko.count_pools
+_orig_visible_pools = ko.visible_pools
+
+
+def _tail_expand_variant(kind):
+    def expand_row(ids, t, kpool, tail=None):
+        if tail is None:
+            return _orig_expand_row(ids, t, kpool)
+        a, e = int(tail[0]), int(tail[1])
+        if kind == "early":
+            a -= 1
+        base = _orig_expand_row(ids, t, kpool)
+        tl = np.full(kpool - 1, -1, np.int32)
+        for j in range(kpool - 1):
+            tok = a + j
+            ok = {"unfiltered": tok < e, "strict": tok < e and tok < t,
+                  "early": tok < e and tok <= t, "front": tok < e and tok <= t}[kind]
+            if ok:
+                tl[j] = tok
+        return np.concatenate([tl, base]) if kind == "front" else np.concatenate([base, tl])
+    return expand_row
+
+
+def _tail_count_ceil(cu_seqlens, kpool, tail=False):
+    return _orig_count_pools(cu_seqlens, kpool, False)
+
+
+def _tail_visibility_uncapped(t, kpool, npools=None):
+    return _orig_visible_pools(t, kpool)
+
+
+TAIL_MUTANTS = {
+    "tail_unfiltered": ("expand_row", _tail_expand_variant("unfiltered")),
+    "tail_strict_filter": ("expand_row", _tail_expand_variant("strict")),
+    "tail_starts_one_early": ("expand_row", _tail_expand_variant("early")),
+    "tail_before_the_pools": ("expand_row", _tail_expand_variant("front")),
+    "tail_partial_pool_kept": ("count_pools", _tail_count_ceil),
+    "tail_visibility_not_capped": ("visible_pools", _tail_visibility_uncapped),
+}
+
+
+def test_unmodified_tail_oracle_passes_battery():
+    assert _tail_battery()
+
+
+@pytest.mark.parametrize("name", sorted(TAIL_MUTANTS))
+def test_tail_mutant_is_caught(name, monkeypatch):
+    import oracle
+    attr, fn = TAIL_MUTANTS[name]
+    monkeypatch.setattr(ko, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    assert not _tail_battery(), f"mutant {name} survived the pins"
