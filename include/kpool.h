@@ -63,27 +63,42 @@ typedef enum {
 /* Message for the last non-OK return on this thread ("" if none). */
 const char *kpool_last_error(void);
 
-/* ABI version (major*100 + minor): 200. */
+/* ABI version (major*100 + minor): 300. */
 int kpool_version(void);
 
+/* Tail mode (flags bit of kpool_count_pools, kpool_pool_keys(_gated),
+ * kpool_score_topk(_noalloc) and kpool_expand; pass the same choice to all of
+ * them).  Megatron-LM PR #8299 "Change" names a "tail append" between pool
+ * expansion and mask filtering but does not define it; this library's reading:
+ * a sequence of L tokens has only its L / kpool full pools (the pool count of
+ * the Atlas tp.rs module doc, seq / kpool), and its remaining L mod kpool
+ * tokens, the tail, are appended to every row's expanded token ids and filtered
+ * causally like them.  Without the flag a trailing partial pool is a pool of its
+ * own and there is no tail. */
+#define KPOOL_FLAG_TAIL 2u
+
 /* Pool bookkeeping on the host (Atlas tp.rs module doc: a sequence of L
- * tokens has L/kpool pools; a trailing partial pool is kept).
- *   cu_pools_host[s] = sum over s' < s of ceil(L_s' / kpool), [nseq + 1]
+ * tokens has L/kpool pools).
+ *   flags            0: ceil(L / kpool) pools, a trailing partial pool kept;
+ *                    KPOOL_FLAG_TAIL: floor(L / kpool), full pools only
+ *   cu_pools_host[s] = sum over s' < s of the pool counts, [nseq + 1] (nullable)
  *   *max_pools_out   = the largest pool count of one sequence (nullable)
  * Returns the total pool count P_tot (>= 0) or a negative kpool_status. */
 int64_t kpool_count_pools(const int32_t *cu_seqlens_host, int32_t nseq, int32_t kpool,
-                          int32_t *cu_pools_host, int32_t *max_pools_out);
+                          uint32_t flags, int32_t *cu_pools_host, int32_t *max_pools_out);
 
 /* Step 1 - pooled keys (Megatron-LM PR #8299 "Mechanism": rows score the
  * pooled keys).  For pool p of sequence s, with n = min(kpool, L_s - p*kpool):
  *   kp[cu_pools[s] + p, d] = bf16_rne( fp32( (sum_j k[cu_seqlens[s] + p*kpool + j, d]) / n ) )
  * where the sum is taken in fp32 in token order starting from +0.
  *   k   bf16 [T, D]  one key per token (the indexer's key projection has no head axis)
- *   kp  bf16 [P_tot, D] output, P_tot from kpool_count_pools
+ *   kp  bf16 [P_tot, D] output, P_tot from kpool_count_pools with the same flags
+ *   flags 0 or KPOOL_FLAG_TAIL (full pools only; cu_pools_dev must count the same way)
  * D must be a multiple of 8 (<= 1024); kpool >= 1. */
 int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host,
                     const int32_t *cu_seqlens_dev, const int32_t *cu_pools_dev,
-                    int32_t nseq, int32_t D, int32_t kpool, uint16_t *kp, void *stream);
+                    int32_t nseq, int32_t D, int32_t kpool, uint32_t flags, uint16_t *kp,
+                    void *stream);
 
 /* Step 1, gated variant - the GLM-5.3 indexer's k-pool compression (Atlas inference
  * docs, glm5next_dsa/tp.rs: the shard plan's indexer tensors include a compression
@@ -99,12 +114,13 @@ int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host,
  *   g    bf16 [T, D]      gate scores (the gate projection's output per token and dim)
  *   ape  fp32 [kpool, D]  slot embeddings
  *   kp   bf16 [P_tot, D]  output, laid out as for kpool_pool_keys
+ * flags: 0 or KPOOL_FLAG_TAIL, as for kpool_pool_keys.
  * k, g, ape and kp must be 16-byte aligned; D a multiple of 8 (<= 1024); kpool >= 1.
  * Inputs must be finite. */
 int kpool_pool_keys_gated(const uint16_t *k, const uint16_t *g, const float *ape,
                           const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                           const int32_t *cu_pools_dev, int32_t nseq, int32_t D, int32_t kpool,
-                          uint16_t *kp, void *stream);
+                          uint32_t flags, uint16_t *kp, void *stream);
 
 /* Workspace for kpool_score_topk over rows [q_lo, q_hi): per query row of a
  * chunk, one fp32 score row at a pitch of max_pools rounded up to 64 plus one
@@ -133,19 +149,22 @@ size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools, int3
  *            (kpool_workspace_bytes(q_lo, q_lo + 1, max_pools, 1)).  Each chunk
  *            has as many rows as the 2 GiB score cap and its buffer allow.
  *            Contents are scratch on return.
- *   flags    0 or KPOOL_FLAG_OVERLAP.  0: one chunk buffer; every launch on the
- *            caller's stream, one after the other (each kernel runs alone, which
- *            per-kernel timing needs).  KPOOL_FLAG_OVERLAP: a workspace of two
- *            rows or more is split into two chunk buffers, and consecutive chunks
- *            alternate between the caller's stream and its helper stream, so one
- *            chunk's selection runs beside the next chunk's scoring; each buffer
- *            keeps the 2 GiB cap.  Results are bitwise the same either way.
- *            Unknown bits return KPOOL_EINVAL.
+ *   flags    KPOOL_FLAG_OVERLAP and/or KPOOL_FLAG_TAIL.  Without OVERLAP: one
+ *            chunk buffer; every launch on the caller's stream, one after the other
+ *            (each kernel runs alone, which per-kernel timing needs).  With
+ *            KPOOL_FLAG_OVERLAP: a workspace of two rows or more is split into two
+ *            chunk buffers, and consecutive chunks alternate between the caller's
+ *            stream and its helper stream, so one chunk's selection runs beside the
+ *            next chunk's scoring; each buffer keeps the 2 GiB cap.  Results are
+ *            bitwise the same either way.  KPOOL_FLAG_TAIL: full pools only (kp
+ *            pooled with the same flag), so a row sees min(t / kpool + 1, L / kpool)
+ *            pools.  Unknown bits return KPOOL_EINVAL.
  *   pool_ids int32 [q_hi - q_lo, budget] output: sequence-local pool ids,
  *            best first by (score desc, pool asc), -1 after the visible pools
  *            run out.  -0.0 ranks equal to +0.0; NaN ranks below -inf.  q, kp and
  *            w must be finite (the score's ReLU does not propagate NaN).
- *   scores_out NULLABLE fp32 [q_hi - q_lo, max_pools]: the fp32 scores the
+ *   scores_out NULLABLE fp32 [q_hi - q_lo, max_pools] (max_pools of
+ *            kpool_count_pools with the same tail flag): the fp32 scores the
  *            selection ranked, -inf where the pool is not visible.
  * Supported (H, D): (4, 16) and (32, 128).  q_lo == q_hi is a no-op.
  * Sizes: one sequence's pooled keys must stay below 4 GiB (fewer than 2^24 pools
@@ -160,7 +179,8 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
 
 /* kpool_score_topk for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, and harnesses that forbid hipMalloc.  Same
- * arguments and results as kpool_score_topk with flags = 0, but the workspace is a
+ * arguments and results as kpool_score_topk (flags: KPOOL_FLAG_TAIL as there;
+ * KPOOL_FLAG_OVERLAP has no effect here) but without a workspace argument: the workspace is a
  * static device array of KPOOL_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library:
  * each GPU the library runs on holds its own copy until the process ends.  The call
  * allocates nothing (no hipMalloc / hipFree, no stream or event creation; the profiler
@@ -176,19 +196,24 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
 int kpool_score_topk_noalloc(const uint16_t *q, const uint16_t *kp, const float *w,
                              const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                              int32_t nseq, int32_t H, int32_t D, int32_t kpool, float scale,
-                             int64_t q_lo, int64_t q_hi, int32_t budget, int32_t *pool_ids,
-                             float *scores_out, void *stream);
+                             int64_t q_lo, int64_t q_hi, int32_t budget, uint32_t flags,
+                             int32_t *pool_ids, float *scores_out, void *stream);
 
 /* Step 3 - expansion and causal filter (Megatron-LM PR #8299 "Change": pool
  * expansion and mask filtering run after the pool ids are known).
  *   token_ids[i - q_lo, b*kpool + j] = p*kpool + j   if p = pool_ids[i - q_lo, b] >= 0
  *                                                    and p*kpool + j <= t(i)
  *                                    = -1            otherwise
- *   pool_ids  int32 [q_hi - q_lo, budget];  token_ids int32 [q_hi - q_lo, budget*kpool]. */
+ *   flags 0 or KPOOL_FLAG_TAIL.  Tail mode appends kpool - 1 slots per row: with
+ *   a = (L / kpool) * kpool for the row's sequence of L tokens,
+ *   token_ids[i - q_lo, budget*kpool + j] = a + j if a + j < L and a + j <= t(i), else -1.
+ *   pool_ids  int32 [q_hi - q_lo, budget];
+ *   token_ids int32 [q_hi - q_lo, budget*kpool (+ kpool - 1 in tail mode)], 16-byte
+ *   aligned when kpool = 4 without tail mode. */
 int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host,
                  const int32_t *cu_seqlens_dev, int32_t nseq, int32_t kpool,
-                 int64_t q_lo, int64_t q_hi, int32_t budget, int32_t *token_ids,
-                 void *stream);
+                 int64_t q_lo, int64_t q_hi, int32_t budget, uint32_t flags,
+                 int32_t *token_ids, void *stream);
 
 /* The selection step alone, over caller-provided fp32 scores (the second
  * half of the chunk loop, exposed so it can be checked on its own).

@@ -193,26 +193,40 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
                 (long long)q_lo, (long long)q_hi, (long long)T);
   if (!kpool::score_supported(H, D))
     return fail(KPOOL_EUNSUPPORTED, "%s: (H=%d, D=%d) not compiled; supported (4,16) and (32,128)", fn, H, D);
-  if (flags & ~(uint32_t)KPOOL_FLAG_OVERLAP)
-    return fail(KPOOL_EINVAL, "%s: unknown flags 0x%x", fn, flags & ~(uint32_t)KPOOL_FLAG_OVERLAP);
+  constexpr uint32_t kKnown = KPOOL_FLAG_OVERLAP | KPOOL_FLAG_TAIL;
+  if (flags & ~kKnown) return fail(KPOOL_EINVAL, "%s: unknown flags 0x%x", fn, flags & ~kKnown);
+  const bool tail = flags & KPOOL_FLAG_TAIL;
   if (q_lo == q_hi) return ok();
-  if (!q || !kp || !w || !cu_seqlens_dev || !pool_ids) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
-  if (!aligned16(q) || !aligned16(kp) || !aligned16(w))
-    return fail(KPOOL_EINVAL, "%s: q, kp and w must be 16-byte aligned", fn);
-
   std::vector<int32_t> cu_pools(nseq + 1);
   int32_t max_pools = 0;
-  kpool_count_pools(cu_seqlens_host, nseq, kpool, cu_pools.data(), &max_pools);
+  kpool_count_pools(cu_seqlens_host, nseq, kpool, tail ? KPOOL_FLAG_TAIL : 0u, cu_pools.data(),
+                    &max_pools);
+  // (kp may be null only when there is no pool to read)
+  if (!q || (!kp && max_pools > 0) || !w || !cu_seqlens_dev || !pool_ids)
+    return fail(KPOOL_EINVAL, "%s: null pointer", fn);
+  if (!aligned16(q) || !aligned16(kp) || !aligned16(w))
+    return fail(KPOOL_EINVAL, "%s: q, kp and w must be 16-byte aligned", fn);
   // The score kernel addresses one sequence's pooled keys and one chunk's score rows
   // with 32-bit byte offsets: a sequence's keys must stay below 4 GiB (16M pools at
   // D = 128) and one score row within the 2 GiB chunk cap.
   if ((int64_t)max_pools * D * 2 > (int64_t)0xFFFFFFFF || pitch_of(max_pools) * 4 > kChunkCapBytes)
     return fail(KPOOL_EUNSUPPORTED, "%s: a sequence of %d pools is beyond the supported size", fn,
                 max_pools);
+  hipStream_t st = (hipStream_t)stream;
+  if (max_pools == 0) {
+    // No sequence has a pool (tail mode, every sequence shorter than kpool): nothing to
+    // score.  The selection kernel reads no score of a row without visible pools and
+    // writes its ids as -1; scores_out has no columns.
+    hipError_t e = timed_if(!use_scratch, 2, st, [&] {
+      return kpool::launch_topk(nullptr, 0, q_hi - q_lo, nullptr, cu_seqlens_dev, nseq, q_lo, kpool,
+                                tail, budget, pool_ids, nullptr, 0, st);
+    });
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return ok();
+  }
   const int64_t ld = pitch_of(max_pools);
   const int64_t ldg = ld / kpool::kGroup;
   const int64_t row_bytes = ws_row_bytes(ld);
-  hipStream_t st = (hipStream_t)stream;
   if (use_scratch) {
     if (row_bytes > (int64_t)kScratchBytes)
       return fail(KPOOL_EWORKSPACE,
@@ -222,7 +236,7 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
     hipError_t e = scratch_ptr(st, &workspace);
     if (e != hipSuccess) return hip_fail(fn, e);
     workspace_bytes = kScratchBytes;
-    flags = 0;
+    flags &= ~(uint32_t)KPOOL_FLAG_OVERLAP;
   }
   if (!workspace || (int64_t)workspace_bytes < row_bytes)
     return fail(KPOOL_EWORKSPACE, "%s: workspace must hold one score row (%lld bytes), got %zu", fn,
@@ -246,14 +260,16 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
   // score + select of rows [c0, c1) into one buffer, on one stream
   auto enqueue_chunk = [&](int64_t c0, int64_t c1, float *ws, float *gws, hipStream_t cs) -> hipError_t {
     // sequences overlapping [c0, c1): one segment each, cut into row tiles
-    struct Seg { int32_t lo, hi, start, pool_base; };
+    struct Seg { int32_t lo, hi, start, pool_base, pool_count; };
     std::vector<Seg> segs;
     int s = (int)(std::upper_bound(cu_seqlens_host, cu_seqlens_host + nseq + 1, (int32_t)c0) -
                   cu_seqlens_host) - 1;
     for (; s < nseq && cu_seqlens_host[s] < c1; ++s) {
       const int64_t lo = std::max<int64_t>(c0, cu_seqlens_host[s]);
       const int64_t hi = std::min<int64_t>(c1, cu_seqlens_host[s + 1]);
-      if (lo < hi) segs.push_back({(int32_t)lo, (int32_t)hi, cu_seqlens_host[s], cu_pools[s]});
+      if (lo < hi)
+        segs.push_back({(int32_t)lo, (int32_t)hi, cu_seqlens_host[s], cu_pools[s],
+                        cu_pools[s + 1] - cu_pools[s]});
     }
     for (size_t g0 = 0; g0 < segs.size(); g0 += kpool::kMaxSegs) {
       kpool::SegList L{};
@@ -266,8 +282,9 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
         L.row_hi[j] = sg.hi;
         L.seq_start[j] = sg.start;
         L.pool_base[j] = sg.pool_base;
+        L.pool_count[j] = sg.pool_count;
         ntiles += (sg.hi - sg.lo + tile_rows - 1) / tile_rows;
-        max_npv = std::max<int32_t>(max_npv, (sg.hi - 1 - sg.start) / kpool + 1);
+        max_npv = std::max<int32_t>(max_npv, std::min((sg.hi - 1 - sg.start) / kpool + 1, sg.pool_count));
       }
       L.tile_start[L.nseg] = ntiles;
       // pool segments per tile: about KPOOL_SCORE_TARGET_WGS workgroups per launch (4 per
@@ -284,13 +301,13 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
       if (e != hipSuccess) return e;
     }
     hipError_t e = timed_if(!use_scratch, 2, cs, [&] {
-      return kpool::launch_topk(ws, ld, c1 - c0, nullptr, cu_seqlens_dev, nseq, c0, kpool, budget,
+      return kpool::launch_topk(ws, ld, c1 - c0, nullptr, cu_seqlens_dev, nseq, c0, kpool, tail, budget,
                                 pool_ids + (c0 - q_lo) * budget, gws, ldg, cs);
     });
     if (e != hipSuccess) return e;
     if (scores_out) {
       e = timed_if(!use_scratch, 4, cs, [&] {
-        return kpool::launch_scores_copy(ws, ld, c1 - c0, cu_seqlens_dev, nseq, c0, kpool,
+        return kpool::launch_scores_copy(ws, ld, c1 - c0, cu_seqlens_dev, nseq, c0, kpool, tail,
                                          scores_out + (c0 - q_lo) * max_pools, max_pools, cs);
       });
     }
@@ -333,19 +350,22 @@ extern "C" {
 
 const char *kpool_last_error(void) { return g_err.c_str(); }
 
-int kpool_version(void) { return 200; }
+int kpool_version(void) { return 300; }
 
 int64_t kpool_count_pools(const int32_t *cu_seqlens_host, int32_t nseq, int32_t kpool,
-                          int32_t *cu_pools_host, int32_t *max_pools_out) {
+                          uint32_t flags, int32_t *cu_pools_host, int32_t *max_pools_out) {
   int rc = check_cu(cu_seqlens_host, nseq, "kpool_count_pools");
   if (rc) return rc;
   if (kpool < 1) return fail(KPOOL_EINVAL, "kpool_count_pools: kpool must be >= 1 (got %d)", kpool);
+  if (flags & ~(uint32_t)KPOOL_FLAG_TAIL)
+    return fail(KPOOL_EINVAL, "kpool_count_pools: unknown flags 0x%x", flags);
+  const bool tail = flags & KPOOL_FLAG_TAIL;
   int64_t tot = 0;
   int32_t mx = 0;
   if (cu_pools_host) cu_pools_host[0] = 0;
   for (int32_t s = 0; s < nseq; ++s) {
     const int64_t L = (int64_t)cu_seqlens_host[s + 1] - cu_seqlens_host[s];
-    const int64_t np = (L + kpool - 1) / kpool;
+    const int64_t np = tail ? L / kpool : (L + kpool - 1) / kpool;
     tot += np;
     mx = std::max<int32_t>(mx, (int32_t)np);
     if (cu_pools_host) cu_pools_host[s + 1] = (int32_t)tot;
@@ -356,14 +376,14 @@ int64_t kpool_count_pools(const int32_t *cu_seqlens_host, int32_t nseq, int32_t 
 }
 
 int kpool_pool_keys(const uint16_t *k, const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
-                    const int32_t *cu_pools_dev, int32_t nseq, int32_t D, int32_t kpool, uint16_t *kp,
-                    void *stream) {
+                    const int32_t *cu_pools_dev, int32_t nseq, int32_t D, int32_t kpool, uint32_t flags,
+                    uint16_t *kp, void *stream) {
   const char *fn = "kpool_pool_keys";
   int rc = check_cu(cu_seqlens_host, nseq, fn);
   if (rc) return rc;
   if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
   if (D < 8 || D > 1024 || D % 8) return fail(KPOOL_EINVAL, "%s: D must be a multiple of 8 in [8, 1024] (got %d)", fn, D);
-  const int64_t P_tot = kpool_count_pools(cu_seqlens_host, nseq, kpool, nullptr, nullptr);
+  const int64_t P_tot = kpool_count_pools(cu_seqlens_host, nseq, kpool, flags, nullptr, nullptr);
   if (P_tot < 0) return (int)P_tot;
   if (P_tot == 0) return ok();
   if (!k || !kp || !cu_seqlens_dev || !cu_pools_dev) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
@@ -397,23 +417,23 @@ int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,
 int kpool_score_topk_noalloc(const uint16_t *q, const uint16_t *kp, const float *w,
                              const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                              int32_t nseq, int32_t H, int32_t D, int32_t kpool, float scale,
-                             int64_t q_lo, int64_t q_hi, int32_t budget, int32_t *pool_ids,
-                             float *scores_out, void *stream) {
+                             int64_t q_lo, int64_t q_hi, int32_t budget, uint32_t flags,
+                             int32_t *pool_ids, float *scores_out, void *stream) {
   return score_topk_impl("kpool_score_topk_noalloc", q, kp, w, cu_seqlens_host, cu_seqlens_dev, nseq,
-                         H, D, kpool, scale, q_lo, q_hi, budget, nullptr, 0, 0, true, pool_ids,
+                         H, D, kpool, scale, q_lo, q_hi, budget, nullptr, 0, flags, true, pool_ids,
                          scores_out, stream);
 }
 
 int kpool_pool_keys_gated(const uint16_t *k, const uint16_t *g, const float *ape,
                           const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                           const int32_t *cu_pools_dev, int32_t nseq, int32_t D, int32_t kpool,
-                          uint16_t *kp, void *stream) {
+                          uint32_t flags, uint16_t *kp, void *stream) {
   const char *fn = "kpool_pool_keys_gated";
   int rc = check_cu(cu_seqlens_host, nseq, fn);
   if (rc) return rc;
   if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
   if (D < 8 || D > 1024 || D % 8) return fail(KPOOL_EINVAL, "%s: D must be a multiple of 8 in [8, 1024] (got %d)", fn, D);
-  const int64_t P_tot = kpool_count_pools(cu_seqlens_host, nseq, kpool, nullptr, nullptr);
+  const int64_t P_tot = kpool_count_pools(cu_seqlens_host, nseq, kpool, flags, nullptr, nullptr);
   if (P_tot < 0) return (int)P_tot;
   if (P_tot == 0) return ok();
   if (!k || !g || !ape || !kp || !cu_seqlens_dev || !cu_pools_dev) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
@@ -430,21 +450,24 @@ int kpool_pool_keys_gated(const uint16_t *k, const uint16_t *g, const float *ape
 
 int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host, const int32_t *cu_seqlens_dev,
                  int32_t nseq, int32_t kpool, int64_t q_lo, int64_t q_hi, int32_t budget,
-                 int32_t *token_ids, void *stream) {
+                 uint32_t flags, int32_t *token_ids, void *stream) {
   const char *fn = "kpool_expand";
   int rc = check_cu(cu_seqlens_host, nseq, fn);
   if (rc) return rc;
   const int64_t T = cu_seqlens_host[nseq];
   if (kpool < 1) return fail(KPOOL_EINVAL, "%s: kpool must be >= 1 (got %d)", fn, kpool);
   if (budget < 1) return fail(KPOOL_EINVAL, "%s: budget must be >= 1 (got %d)", fn, budget);
+  if (flags & ~(uint32_t)KPOOL_FLAG_TAIL) return fail(KPOOL_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  const bool tail = flags & KPOOL_FLAG_TAIL;
   if (q_lo < 0 || q_lo > q_hi || q_hi > T)
     return fail(KPOOL_EINVAL, "%s: need 0 <= q_lo <= q_hi <= T", fn);
   if (q_lo == q_hi) return ok();
   if (!pool_ids || !token_ids || !cu_seqlens_dev) return fail(KPOOL_EINVAL, "%s: null pointer", fn);
-  if (kpool == 4 && !aligned16(token_ids)) return fail(KPOOL_EINVAL, "%s: token_ids must be 16-byte aligned", fn);
+  if (kpool == 4 && !tail && !aligned16(token_ids))
+    return fail(KPOOL_EINVAL, "%s: token_ids must be 16-byte aligned", fn);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(3, st, [&] {
-    return kpool::launch_expand(pool_ids, cu_seqlens_dev, nseq, kpool, q_lo, q_hi - q_lo, budget,
+    return kpool::launch_expand(pool_ids, cu_seqlens_dev, nseq, kpool, tail, q_lo, q_hi - q_lo, budget,
                                 token_ids, st);
   });
   if (e != hipSuccess) return hip_fail(fn, e);
@@ -464,7 +487,7 @@ int kpool_topk(const float *scores, int64_t ld, const int32_t *n_valid, int64_t 
   if (rows > 0x7FFFFFFF) return fail(KPOOL_EINVAL, "%s: too many rows", fn);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(2, st, [&] {
-    return kpool::launch_topk(scores, ld, rows, n_valid, nullptr, 0, 0, 1, budget, pool_ids,
+    return kpool::launch_topk(scores, ld, rows, n_valid, nullptr, 0, 0, 1, false, budget, pool_ids,
                               nullptr, 0, st);
   });
   if (e != hipSuccess) return hip_fail(fn, e);

@@ -6,6 +6,11 @@
 // payload).  Keeping a filtered slot in place as -1 and int32 token ids are
 // this library's reading.
 //
+// Tail mode (a reading of the pages' "tail append", named between expansion and mask
+// filtering in the same passage): the sequence's L mod kpool tokens after its last
+// full pool are appended after a row's budget*kpool slots, in kpool - 1 more slots,
+// and filtered like the rest (-1 where absent or after the row).
+//
 // HBM-bound: workgroups stride over rows (one sequence lookup per row), threads over
 // a row's slots.  kpool == 4: each slot is one 16-byte store; kpool == 1 with 16-byte
 // aligned rows: 4 slots per thread through 16-byte loads and stores; otherwise one
@@ -20,15 +25,36 @@ constexpr int kExpandMaxBlocks = 65536;
 
 __global__ __launch_bounds__(kExpandThreads) void expand_kernel(const int32_t *__restrict__ pool_ids,
                                                                 const int32_t *__restrict__ cu_seqlens,
-                                                                int nseq, int kpool, int64_t q_lo,
-                                                                int64_t nrows, int budget, bool vec,
+                                                                int nseq, int kpool, bool tail,
+                                                                int64_t q_lo, int64_t nrows,
+                                                                int budget, bool vec,
                                                                 int32_t *__restrict__ tok) {
+  const int ntail = tail ? kpool - 1 : 0;
+  const int64_t width = (int64_t)budget * kpool + ntail;
   for (int64_t r = blockIdx.x; r < nrows; r += gridDim.x) {
     const int64_t i = q_lo + r;
     const int s = find_seq(cu_seqlens, nseq, i);
     const int64_t t = i - cu_seqlens[s];
     const int32_t *prow = pool_ids + r * budget;
-    int32_t *orow = tok + r * budget * kpool;
+    int32_t *orow = tok + r * width;
+    if (tail) {  // rows of odd width: one slot per thread, then the tail
+      const int64_t L = cu_seqlens[s + 1] - cu_seqlens[s];
+      const int64_t a = L / kpool * kpool;  // the tail's first token
+      for (int64_t e = threadIdx.x; e < width; e += kExpandThreads) {
+        int64_t tk;
+        bool ok;
+        if (e < (int64_t)budget * kpool) {
+          const int32_t p = prow[e / kpool];
+          tk = (int64_t)p * kpool + e % kpool;
+          ok = p >= 0;
+        } else {
+          tk = a + (e - (int64_t)budget * kpool);
+          ok = tk < L;
+        }
+        orow[e] = (ok && tk <= t) ? (int32_t)tk : -1;
+      }
+      continue;
+    }
     // The 16-byte token-id stores are non-temporal: the output is written once and not
     // read again on the path.
     typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -65,13 +91,13 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(const int32_t *_
 }  // namespace
 
 hipError_t launch_expand(const int32_t *pool_ids, const int32_t *cu_seqlens, int32_t nseq,
-                         int32_t kpool, int64_t q_lo, int64_t nrows, int32_t budget,
+                         int32_t kpool, bool tail, int64_t q_lo, int64_t nrows, int32_t budget,
                          int32_t *token_ids, hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
   const bool vec = budget % 4 == 0 && ((uintptr_t)pool_ids % 16) == 0 && ((uintptr_t)token_ids % 16) == 0;
   const unsigned blocks = (unsigned)(nrows < kExpandMaxBlocks ? nrows : kExpandMaxBlocks);
   hipLaunchKernelGGL(expand_kernel, dim3(blocks), dim3(kExpandThreads), 0, stream, pool_ids,
-                     cu_seqlens, nseq, kpool, q_lo, nrows, budget, vec, token_ids);
+                     cu_seqlens, nseq, kpool, tail, q_lo, nrows, budget, vec, token_ids);
   return hipGetLastError();
 }
 

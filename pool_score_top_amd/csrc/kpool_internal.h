@@ -23,6 +23,7 @@ struct SegList {
   int32_t row_hi[kMaxSegs];          // one past the last global row
   int32_t seq_start[kMaxSegs];       // global row of the sequence's token 0
   int32_t pool_base[kMaxSegs];       // first pooled-key row of the sequence
+  int32_t pool_count[kMaxSegs];      // pools of the sequence (caps every row's visible count)
 };
 
 // ----------------------------------------------------------------------------
@@ -52,27 +53,36 @@ constexpr int kTopkMaxBudget = 2048;
 // Rows [row0, row0 + nrows) of `scores` (row r at scores + r*ld).  The number
 // of ranked entries of row r is n_valid[r] if n_valid is not null, else
 // (t / kpool + 1) for the row's sequence-local position t (global row
-// grow0 + r looked up in cu_seqlens).
+// grow0 + r looked up in cu_seqlens), capped at L / kpool for a sequence of L
+// tokens in tail mode (full pools only).
 // With gmax (the score kernel's 16-pool group maxima, row pitch ldg) the selection reads
 // the group maxima first and then only the groups that can hold a winner; without it
 // every row is read in full.
 hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
                        const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
-                       int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
+                       bool tail, int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
                        hipStream_t stream);
 
 hipError_t launch_scores_copy(const float *ws, int64_t ld, int64_t nrows, const int32_t *cu_seqlens,
-                              int32_t nseq, int64_t grow0, int32_t kpool, float *dst,
+                              int32_t nseq, int64_t grow0, int32_t kpool, bool tail, float *dst,
                               int64_t dst_ld, hipStream_t stream);
 
+// tail: full pools only, and kpool - 1 tail slots after a row's budget*kpool expanded ones
 hipError_t launch_expand(const int32_t *pool_ids, const int32_t *cu_seqlens, int32_t nseq,
-                         int32_t kpool, int64_t q_lo, int64_t nrows, int32_t budget,
+                         int32_t kpool, bool tail, int64_t q_lo, int64_t nrows, int32_t budget,
                          int32_t *token_ids, hipStream_t stream);
 
 // ----------------------------------------------------------------------------
 // Device helpers
 // ----------------------------------------------------------------------------
 #if defined(__HIPCC__)
+
+// Pools visible to the row at sequence-local position t of a sequence of L tokens:
+// p*kpool <= t, and in tail mode (full pools only) p < L / kpool.
+__device__ inline int64_t visible_count(int64_t t, int64_t L, int kpool, bool tail) {
+  const int64_t n = t / kpool + 1;
+  return tail ? min(n, L / kpool) : n;
+}
 
 // Index of the sequence holding global row `row`: the largest s < nseq with
 // cu[s] <= row (empty sequences are skipped because their start repeats).

@@ -95,7 +95,9 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   const int64_t row0 = (int64_t)segs.row_lo[g] + (int64_t)(tile - segs.tile_start[g]) * kTileRows;
   const int nrows = (int)min<int64_t>(kTileRows, segs.row_hi[g] - row0);
   const int64_t t0 = row0 - segs.seq_start[g];
-  const int npv = (int)((t0 + nrows - 1) / kpool) + 1;  // pools visible to the tile's last row
+  // pools visible to the tile's last row (at most the sequence's pool count, which only
+  // tail mode's full-pool count can undercut); each row's own limit below is capped by it
+  const int npv = min((int)((t0 + nrows - 1) / kpool) + 1, segs.pool_count[g]);
   const int p_begin = pseg * pseg_pools;
   if (p_begin >= npv) return;  // whole workgroup leaves together
   const int p_end = min(npv, p_begin + pseg_pools);

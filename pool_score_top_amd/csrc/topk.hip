@@ -314,7 +314,8 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
                                                         const int32_t *__restrict__ n_valid,
                                                         const int32_t *__restrict__ cu_seqlens,
                                                         int nseq, int64_t grow0, int kpool,
-                                                        int budget, int32_t *__restrict__ out,
+                                                        bool tail, int budget,
+                                                        int32_t *__restrict__ out,
                                                         const float *__restrict__ gmax,
                                                         int64_t ldg) {
   constexpr int kThreads = Cfg<NMAX>::kThreads;
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
   } else {
     const int64_t i = grow0 + r;
     const int s = find_seq(cu_seqlens, nseq, i);
-    n = (i - cu_seqlens[s]) / kpool + 1;
+    n = visible_count(i - cu_seqlens[s], cu_seqlens[s + 1] - cu_seqlens[s], kpool, tail);
   }
   const float *row = scores + r * ld;
   const float *grow = GMAX ? gmax + r * ldg : nullptr;
@@ -621,11 +622,12 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
 __global__ __launch_bounds__(256) void scores_copy_kernel(const float *__restrict__ ws, int64_t ld,
                                                           const int32_t *__restrict__ cu_seqlens,
                                                           int nseq, int64_t grow0, int kpool,
-                                                          float *__restrict__ dst, int64_t dst_ld) {
+                                                          bool tail, float *__restrict__ dst,
+                                                          int64_t dst_ld) {
   const int64_t r = blockIdx.x;
   const int64_t i = grow0 + r;
   const int s = find_seq(cu_seqlens, nseq, i);
-  const int64_t n = (i - cu_seqlens[s]) / kpool + 1;
+  const int64_t n = visible_count(i - cu_seqlens[s], cu_seqlens[s + 1] - cu_seqlens[s], kpool, tail);
   const float ninf = __uint_as_float(0xFF800000u);
   for (int64_t p = threadIdx.x; p < dst_ld; p += blockDim.x)
     dst[r * dst_ld + p] = p < n ? ws[r * ld + p] : ninf;
@@ -636,42 +638,44 @@ __global__ __launch_bounds__(256) void scores_copy_kernel(const float *__restric
 template <bool GMAX, int NMAX>
 static void launch_topk_inst(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
                              const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
-                             int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
+                             bool tail, int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
                              hipStream_t stream) {
   hipLaunchKernelGGL((topk_kernel<GMAX, NMAX>), dim3((unsigned)nrows), dim3(Cfg<NMAX>::kThreads), 0,
-                     stream, scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, budget, out, gmax,
-                     ldg);
+                     stream, scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, tail, budget, out,
+                     gmax, ldg);
 }
 
 hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
                        const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
-                       int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
+                       bool tail, int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
                        hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
   if (budget > kTopkMaxBudget) return hipErrorInvalidValue;
   // budgets above 512 need more maxima per thread for a tight bound (and longer lists)
   const bool big = budget > 512;
   if (gmax && big)
-    launch_topk_inst<true, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, budget,
+    launch_topk_inst<true, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
+                              budget,
                               out, gmax, ldg, stream);
   else if (gmax)
-    launch_topk_inst<true, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool,
-                                       budget, out, gmax, ldg, stream);
+    launch_topk_inst<true, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
+                              budget, out, gmax, ldg, stream);
   else if (big)
-    launch_topk_inst<false, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, budget,
+    launch_topk_inst<false, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
+                              budget,
                                out, gmax, ldg, stream);
   else
-    launch_topk_inst<false, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool,
-                                        budget, out, gmax, ldg, stream);
+    launch_topk_inst<false, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
+                              budget, out, gmax, ldg, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_scores_copy(const float *ws, int64_t ld, int64_t nrows, const int32_t *cu_seqlens,
-                              int32_t nseq, int64_t grow0, int32_t kpool, float *dst,
+                              int32_t nseq, int64_t grow0, int32_t kpool, bool tail, float *dst,
                               int64_t dst_ld, hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
   hipLaunchKernelGGL(scores_copy_kernel, dim3((unsigned)nrows), dim3(256), 0, stream, ws, ld,
-                     cu_seqlens, nseq, grow0, kpool, dst, dst_ld);
+                     cu_seqlens, nseq, grow0, kpool, tail, dst, dst_ld);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libkpool.so")
 
 KPOOL_OK, KPOOL_EINVAL, KPOOL_EUNSUPPORTED, KPOOL_EWORKSPACE, KPOOL_EHIP = 0, -1, -2, -3, -4
 KPOOL_FLAG_OVERLAP = 1
+KPOOL_FLAG_TAIL = 2
 PROFILE_KINDS = ("pool_keys", "score", "topk", "expand", "scores_copy")
 
 _lib = None
@@ -38,18 +39,19 @@ def lib():
         raise RuntimeError(f"libkpool.so is not built ({LIB_PATH}); run __graft_entry__.build()")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    u32 = ctypes.c_uint32
     sig = {
         "kpool_last_error": (ctypes.c_char_p, []),
         "kpool_version": (ctypes.c_int, []),
-        "kpool_count_pools": (i64, [vp, i32, i32, vp, vp]),
-        "kpool_pool_keys": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
-        "kpool_pool_keys_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "kpool_count_pools": (i64, [vp, i32, i32, u32, vp, vp]),
+        "kpool_pool_keys": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, u32, vp, vp]),
+        "kpool_pool_keys_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, u32, vp, vp]),
         "kpool_workspace_bytes": (sz, [i64, i64, i32, i32]),
         "kpool_score_topk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i64, i64,
-                                            i32, vp, sz, ctypes.c_uint32, vp, vp, vp]),
+                                            i32, vp, sz, u32, vp, vp, vp]),
         "kpool_score_topk_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
-                                                    i64, i64, i32, vp, vp, vp]),
-        "kpool_expand": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, i64, i32, vp, vp]),
+                                                    i64, i64, i32, u32, vp, vp, vp]),
+        "kpool_expand": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, i64, i32, u32, vp, vp]),
         "kpool_topk": (ctypes.c_int, [vp, i64, vp, i64, i32, vp, vp]),
         "kpool_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "kpool_profile_collect": (ctypes.c_int, [vp, vp]),
@@ -113,13 +115,17 @@ def version() -> int:
     return lib().kpool_version()
 
 
-def count_pools(cu_seqlens, kpool: int):
-    """(cu_pools int32 [nseq+1], max_pools, P_tot) for a host cu_seqlens."""
+def _tail(tail):
+    return KPOOL_FLAG_TAIL if tail else 0
+
+
+def count_pools(cu_seqlens, kpool: int, tail: bool = False):
+    """(cu_pools int32 [nseq+1], max_pools, P_tot) for a host cu_seqlens (tail: full pools)."""
     cu, cup = _host_i32(cu_seqlens)
     nseq = len(cu) - 1
     out = np.zeros(max(nseq, 0) + 1, dtype=np.int32)
     mx = ctypes.c_int32(0)
-    tot = lib().kpool_count_pools(cup, nseq, kpool, out.ctypes.data_as(ctypes.c_void_p),
+    tot = lib().kpool_count_pools(cup, nseq, kpool, _tail(tail), out.ctypes.data_as(ctypes.c_void_p),
                                   ctypes.byref(mx))
     _check(0 if tot >= 0 else tot, "kpool_count_pools")
     return out, int(mx.value), int(tot)
@@ -131,24 +137,25 @@ def workspace_bytes(q_lo: int, q_hi: int, max_pools: int, nbuf: int = 2) -> int:
     return int(lib().kpool_workspace_bytes(q_lo, q_hi, max_pools, nbuf))
 
 
-def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None, stream=None):
+def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None, stream=None,
+              tail: bool = False):
     import torch
     _need(k, "k", 2)
     cu, cup = _host_i32(cu_seqlens)
     nseq = len(cu) - 1
-    _, _, P_tot = count_pools(cu, kpool)
+    _, _, P_tot = count_pools(cu, kpool, tail)
     D = k.shape[-1]
     if out is None:
         with _on(stream):
             out = torch.empty((P_tot, D), dtype=k.dtype, device=k.device)
     rc = lib().kpool_pool_keys(_p(k), cup, _p(cu_seqlens_dev), _p(cu_pools_dev), nseq, D, kpool,
-                               _p(out), _stream(stream))
+                               _tail(tail), _p(out), _stream(stream))
     _check(rc, "kpool_pool_keys")
     return out
 
 
 def pool_keys_gated(k, g, ape, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None,
-                    stream=None):
+                    stream=None, tail: bool = False):
     """Gated pooled keys: k, g bf16 [T, D] (int16 storage), ape fp32 [kpool, D]."""
     import torch
     _need(k, "k", 2)
@@ -156,7 +163,7 @@ def pool_keys_gated(k, g, ape, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: 
     _need(ape, "ape", dtype=torch.float32)
     cu, cup = _host_i32(cu_seqlens)
     nseq = len(cu) - 1
-    _, _, P_tot = count_pools(cu, kpool)
+    _, _, P_tot = count_pools(cu, kpool, tail)
     D = k.shape[-1]
     if tuple(g.shape) != tuple(k.shape) or tuple(ape.shape) != (kpool, D):
         raise ValueError("need g shaped like k and ape [kpool, D]")
@@ -164,7 +171,7 @@ def pool_keys_gated(k, g, ape, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: 
         with _on(stream):
             out = torch.empty((P_tot, D), dtype=k.dtype, device=k.device)
     rc = lib().kpool_pool_keys_gated(_p(k), _p(g), _p(ape), cup, _p(cu_seqlens_dev), _p(cu_pools_dev),
-                                     nseq, D, kpool, _p(out), _stream(stream))
+                                     nseq, D, kpool, _tail(tail), _p(out), _stream(stream))
     _check(rc, "kpool_pool_keys_gated")
     return out
 
@@ -172,7 +179,7 @@ def pool_keys_gated(k, g, ape, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: 
 def score_topk(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_lo: int = 0,
                q_hi: int | None = None, scale: float | None = None, workspace=None,
                pool_ids=None, scores_out=None, want_scores: bool = False, overlap: bool = False,
-               stream=None):
+               stream=None, tail: bool = False):
     """Run the chunked score + top-k for rows [q_lo, q_hi).  Returns (pool_ids, scores_out).
 
     overlap=True passes KPOOL_FLAG_OVERLAP (two chunk buffers on two streams); a
@@ -189,7 +196,7 @@ def score_topk(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_
     H, D = q.shape[-2], q.shape[-1]
     if scale is None:
         scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
-    _, max_pools, _ = count_pools(cu, kpool)
+    _, max_pools, _ = count_pools(cu, kpool, tail)
     rows = max(0, q_hi - q_lo)
     with _on(stream):
         if pool_ids is None:
@@ -202,7 +209,7 @@ def score_topk(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_
     rc = lib().kpool_score_topk(_p(q), _p(kp), _p(w), cup, _p(cu_seqlens_dev), nseq, H, D, kpool,
                                 ctypes.c_float(scale), q_lo, q_hi, budget, _p(workspace),
                                 workspace.numel() * workspace.element_size(),
-                                KPOOL_FLAG_OVERLAP if overlap else 0, _p(pool_ids),
+                                (KPOOL_FLAG_OVERLAP if overlap else 0) | _tail(tail), _p(pool_ids),
                                 _p(scores_out), _stream(stream))
     _check(rc, "kpool_score_topk")
     return pool_ids, scores_out
@@ -210,7 +217,7 @@ def score_topk(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_
 
 def score_topk_noalloc(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int,
                        q_lo: int, q_hi: int, pool_ids, scores_out=None, scale: float | None = None,
-                       stream=None):
+                       stream=None, tail: bool = False):
     """score_topk through the library's static scratch (kpool_score_topk_noalloc): the
     caller passes every output; nothing is allocated here or in the library."""
     import torch
@@ -223,13 +230,14 @@ def score_topk_noalloc(q, kp, w, cu_seqlens, cu_seqlens_dev, kpool: int, budget:
         scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
     rc = lib().kpool_score_topk_noalloc(_p(q), _p(kp), _p(w), cup, _p(cu_seqlens_dev), len(cu) - 1,
                                         H, D, kpool, ctypes.c_float(scale), q_lo, q_hi, budget,
-                                        _p(pool_ids), _p(scores_out), _stream(stream))
+                                        _tail(tail), _p(pool_ids), _p(scores_out), _stream(stream))
     _check(rc, "kpool_score_topk_noalloc")
     return pool_ids, scores_out
 
 
 def expand(pool_ids, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_lo: int = 0,
-           q_hi: int | None = None, out=None, stream=None):
+           q_hi: int | None = None, out=None, stream=None, tail: bool = False):
+    """Token ids [rows, budget*kpool] (+ kpool - 1 tail slots in tail mode)."""
     import torch
     cu, cup = _host_i32(cu_seqlens)
     nseq = len(cu) - 1
@@ -238,9 +246,10 @@ def expand(pool_ids, cu_seqlens, cu_seqlens_dev, kpool: int, budget: int, q_lo: 
     rows = max(0, q_hi - q_lo)
     if out is None:
         with _on(stream):
-            out = torch.empty((rows, budget * kpool), dtype=torch.int32, device=pool_ids.device)
+            out = torch.empty((rows, budget * kpool + (kpool - 1 if tail else 0)), dtype=torch.int32,
+                              device=pool_ids.device)
     rc = lib().kpool_expand(_p(pool_ids), cup, _p(cu_seqlens_dev), nseq, kpool, q_lo, q_hi, budget,
-                            _p(out), _stream(stream))
+                            _tail(tail), _p(out), _stream(stream))
     _check(rc, "kpool_expand")
     return out
 
@@ -281,12 +290,12 @@ class Selector:
     for the row range; `run` enqueues the three library calls on one stream.
     overlap=True (the default) sizes the workspace for two chunk buffers and runs
     the chunk loop with KPOOL_FLAG_OVERLAP; workspace_cap caps the workspace
-    (smaller chunks).
+    (smaller chunks); tail=True runs every step in tail mode (KPOOL_FLAG_TAIL).
     """
 
     def __init__(self, cu_seqlens, kpool: int, budget: int, H: int, D: int, device="cuda",
                  q_lo: int = 0, q_hi: int | None = None, workspace_cap: int | None = None,
-                 scale: float | None = None, overlap: bool = True):
+                 scale: float | None = None, overlap: bool = True, tail: bool = False):
         import torch
         self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
         self.T = int(self.cu[-1])
@@ -294,7 +303,8 @@ class Selector:
         self.q_lo = q_lo
         self.q_hi = self.T if q_hi is None else q_hi
         self.overlap = overlap
-        self.cu_pools, self.max_pools, self.P_tot = count_pools(self.cu, kpool)
+        self.tail = tail
+        self.cu_pools, self.max_pools, self.P_tot = count_pools(self.cu, kpool, tail)
         self.cu_dev = torch.from_numpy(self.cu).to(device)
         self.cu_pools_dev = torch.from_numpy(self.cu_pools).to(device)
         self.scale = float(np.float32(1.0) / np.sqrt(np.float32(D))) if scale is None else scale
@@ -305,7 +315,8 @@ class Selector:
         rows = self.q_hi - self.q_lo
         self.kp = torch.empty((self.P_tot, D), dtype=torch.int16, device=device)
         self.pool_ids = torch.empty((rows, budget), dtype=torch.int32, device=device)
-        self.token_ids = torch.empty((rows, budget * kpool), dtype=torch.int32, device=device)
+        self.token_ids = torch.empty((rows, budget * kpool + (kpool - 1 if tail else 0)),
+                                     dtype=torch.int32, device=device)
 
     @property
     def workspace_bytes(self) -> int:
@@ -326,13 +337,13 @@ class Selector:
         overlap = self.overlap if overlap is None else overlap
         if g is not None:
             pool_keys_gated(k, g, ape, self.cu, self.cu_dev, self.cu_pools_dev, self.kpool,
-                            out=self.kp, stream=stream)
+                            out=self.kp, stream=stream, tail=self.tail)
         else:
             pool_keys(k, self.cu, self.cu_dev, self.cu_pools_dev, self.kpool, out=self.kp,
-                      stream=stream)
+                      stream=stream, tail=self.tail)
         score_topk(q, self.kp, w, self.cu, self.cu_dev, self.kpool, self.budget, self.q_lo, self.q_hi,
                    scale=self.scale, workspace=self.workspace, pool_ids=self.pool_ids,
-                   scores_out=scores_out, overlap=overlap, stream=stream)
+                   scores_out=scores_out, overlap=overlap, stream=stream, tail=self.tail)
         expand(self.pool_ids, self.cu, self.cu_dev, self.kpool, self.budget, self.q_lo, self.q_hi,
-               out=self.token_ids, stream=stream)
+               out=self.token_ids, stream=stream, tail=self.tail)
         return {"kp": self.kp, "pool_ids": self.pool_ids, "token_ids": self.token_ids}

@@ -133,7 +133,7 @@ def fp32_error_bound(q_bits, w, kp_bits, cu_pools, seq, t, kpool, D, H, width):
 
 def check_topk_self(g_scores, g_ids, nvis, budget, where=""):
     for r in range(len(nvis)):
-        want = lexsort_first(g_scores[r, :int(nvis[r])], budget)
+        want = lexsort_first(g_scores[r, :int(nvis[r])], budget)  # (all -1 for a row with none)
         if not np.array_equal(want, g_ids[r]):
             bad = np.nonzero(want != g_ids[r])[0][:5]
             raise AssertionError(f"{where} row {r}: top-k differs from its own scores at slots "
@@ -158,6 +158,8 @@ def check_selection_vs_oracle(g_ids, o_scores, nvis, budget, where=""):
         sel = ids[ids >= 0]
         assert len(sel) == min(n, budget), f"{where} row {r}: {len(sel)} ids, want {min(n, budget)}"
         assert np.all(ids[len(sel):] == -1), f"{where} row {r}: padding not at the tail"
+        if n == 0:          # no visible pool (tail mode, a sequence shorter than kpool)
+            continue
         assert len(np.unique(sel)) == len(sel), f"{where} row {r}: duplicate ids"
         assert sel.max() < n, f"{where} row {r}: id beyond the visible pools"
         want = oracle.select_row(o, budget)
@@ -221,7 +223,7 @@ def oracle_rows(inputs, kpool, rows, kp=None, width=None):
     return kp, s, t
 
 
-def gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool, u=2.0 ** -53):
+def gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool, u=2.0 ** -53, tail=False):
     """Bounds [lo, hi] (fp32 values of bf16 numbers) that the GPU's gated pooled keys may take.
 
     vals: the oracle's fp64 values of the gated pooled keys.  The GPU evaluates the
@@ -240,11 +242,11 @@ def gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool, u=2.0 ** -53):
     g = O.bf16_to_f32(g_bits).astype(np.float64)
     a = np.asarray(ape, np.float32).astype(np.float64)
     cu = np.asarray(cu_seqlens, np.int64)
-    cu_pools, _ = O.count_pools(cu, kpool)
+    cu_pools, _ = O.count_pools(cu, kpool, tail)
     delta = np.zeros_like(vals)
     for s in range(len(cu) - 1):
         start, L = int(cu[s]), int(cu[s + 1] - cu[s])
-        P = (L + kpool - 1) // kpool
+        P = int(cu_pools[s + 1] - cu_pools[s])
         for j0 in range(0, P, 4096):                       # pools in blocks, vectorised
             ps = np.arange(j0, min(P, j0 + 4096))
             for n in np.unique(np.minimum(kpool, L - ps * kpool)):
@@ -261,10 +263,10 @@ def gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool, u=2.0 ** -53):
     return lo, hi, lo != hi
 
 
-def check_gated_keys(gpu_bits, vals, k_bits, g_bits, ape, cu_seqlens, kpool, where=""):
+def check_gated_keys(gpu_bits, vals, k_bits, g_bits, ape, cu_seqlens, kpool, where="", tail=False):
     """The GPU's gated pooled keys against the oracle's values (rule in gated_allowed)."""
     import oracle as O
-    lo, hi, amb = gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool)
+    lo, hi, amb = gated_allowed(vals, k_bits, g_bits, ape, cu_seqlens, kpool, tail=tail)
     got = O.bf16_to_f32(gpu_bits)
     bad = (got < lo) | (got > hi)
     assert not bad.any(), (f"{where}: {bad.sum()} gated keys outside the error bound, first at "

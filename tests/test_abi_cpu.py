@@ -38,12 +38,15 @@ def test_no_process_wide_switch_in_the_header():
     """Every setting is an argument of the call: the header declares no setter."""
     names = declared_functions()
     assert not [n for n in names if "set_" in n], names
-    assert K.version() == 200
+    assert K.version() == 300
 
 
 def test_count_pools_and_workspace():
     cu_pools, mx, tot = K.count_pools([0, 9, 9, 37], 4)
     assert cu_pools.tolist() == [0, 3, 3, 10] and mx == 7 and tot == 10
+    # tail mode: full pools only (9 -> 2, 28 -> 7, a 3-token sequence -> none)
+    cu_pools, mx, tot = K.count_pools([0, 9, 9, 37, 40], 4, tail=True)
+    assert cu_pools.tolist() == [0, 2, 2, 9, 9] and mx == 7 and tot == 9
     # 512k tokens, kpool 4: pitch 131072 floats = 512 KiB per row -> 4096 rows per 2 GiB chunk,
     # plus one fp32 group maximum per 16 pools of each row; two chunk buffers when the
     # range needs more than one chunk
@@ -89,7 +92,7 @@ def _call_score(**kw):
     (dict(cu=[1, 64]), K.KPOOL_EINVAL),
     (dict(cu=[0, 40, 30, 64]), K.KPOOL_EINVAL),
     (dict(nseq=0), K.KPOOL_EINVAL),
-    (dict(flags=2), K.KPOOL_EINVAL),         # unknown flag bit
+    (dict(flags=4), K.KPOOL_EINVAL),         # unknown flag bit (1 overlap, 2 tail)
     (dict(flags=0x80000001), K.KPOOL_EINVAL),
     # one sequence whose pooled keys exceed the kernel's 32-bit byte offsets (2^24 pools at D=128)
     (dict(cu=[0, 1 << 24], kpool=1, H=32, D=128), K.KPOOL_EUNSUPPORTED),
@@ -109,15 +112,41 @@ def test_other_entry_points_reject_bad_arguments():
     vp = ctypes.c_void_p
     cu = np.array([0, 64], dtype=np.int32)
     cup = cu.ctypes.data_as(vp)
-    assert L.kpool_pool_keys(vp(16), cup, vp(16), vp(16), 1, 12, 4, vp(16), None) == K.KPOOL_EINVAL
-    assert L.kpool_pool_keys(vp(16), cup, vp(16), vp(16), 1, 16, 0, vp(16), None) == K.KPOOL_EINVAL
-    assert L.kpool_pool_keys(None, cup, vp(16), vp(16), 1, 16, 4, vp(16), None) == K.KPOOL_EINVAL
-    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 3, 2, 4, vp(16), None) == K.KPOOL_EINVAL
-    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 0, 65, 4, vp(16), None) == K.KPOOL_EINVAL
-    assert L.kpool_expand(None, cup, vp(16), 1, 4, 0, 64, 4, vp(16), None) == K.KPOOL_EINVAL
-    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 0, 64, 4, vp(8), None) == K.KPOOL_EINVAL
+    assert L.kpool_pool_keys(vp(16), cup, vp(16), vp(16), 1, 12, 4, 0, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_pool_keys(vp(16), cup, vp(16), vp(16), 1, 16, 0, 0, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_pool_keys(None, cup, vp(16), vp(16), 1, 16, 4, 0, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_pool_keys(vp(16), cup, vp(16), vp(16), 1, 16, 4, 1, vp(16), None) == K.KPOOL_EINVAL  # flag
+    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 3, 2, 4, 0, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 0, 65, 4, 0, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(None, cup, vp(16), 1, 4, 0, 64, 4, 0, vp(16), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 0, 64, 4, 0, vp(8), None) == K.KPOOL_EINVAL
+    assert L.kpool_expand(vp(16), cup, vp(16), 1, 4, 0, 64, 4, 1, vp(16), None) == K.KPOOL_EINVAL   # flag
     assert L.kpool_topk(vp(16), 6, vp(16), 3, 4, vp(16), None) == K.KPOOL_EINVAL      # ld % 4
     assert L.kpool_topk(vp(16), 8, vp(16), 3, 0, vp(16), None) == K.KPOOL_EINVAL      # budget
     assert L.kpool_topk(vp(8), 8, vp(16), 3, 4, vp(16), None) == K.KPOOL_EINVAL       # alignment
     assert L.kpool_topk(None, 8, vp(16), 0, 4, None, None) == K.KPOOL_OK              # no rows
-    assert L.kpool_count_pools(cup, 1, 0, None, None) == K.KPOOL_EINVAL
+    assert L.kpool_count_pools(cup, 1, 0, 0, None, None) == K.KPOOL_EINVAL
+    assert L.kpool_count_pools(cup, 1, 4, 1, None, None) == K.KPOOL_EINVAL           # overlap flag
+    assert L.kpool_count_pools(cup, 1, 4, 2, None, None) == 16                        # tail: 64 // 4
+
+
+def test_gated_pool_keys_rejects_bad_arguments():
+    L = K.lib()
+    vp = ctypes.c_void_p
+    cu = np.array([0, 64], dtype=np.int32)
+    cup = cu.ctypes.data_as(vp)
+    ok = dict(k=16, g=16, ape=16, cud=16, cpd=16, D=16, kpool=4, flags=0, kp=16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.kpool_pool_keys_gated(vp(a["k"]), vp(a["g"]), vp(a["ape"]), cup, vp(a["cud"]),
+                                       vp(a["cpd"]), 1, a["D"], a["kpool"], a["flags"], vp(a["kp"]), None)
+    for kw in (dict(g=0), dict(ape=0), dict(k=0), dict(kp=0), dict(g=8), dict(ape=4), dict(D=12),
+               dict(kpool=0), dict(flags=1)):
+        assert call(**kw) == K.KPOOL_EINVAL, kw
+        assert K.lib().kpool_last_error().decode()
+    # an empty batch needs no pointers
+    cu0 = np.array([0, 0], dtype=np.int32)
+    assert L.kpool_pool_keys_gated(None, None, None, cu0.ctypes.data_as(vp), None, None, 1, 16, 4, 0,
+                                   None, None) == K.KPOOL_OK

@@ -61,13 +61,15 @@ def test_noalloc_rejects_rows_beyond_the_scratch():
     vp = ctypes.c_void_p
     cu = np.array([0, 16_000_000], dtype=np.int32)
     rc = L.kpool_score_topk_noalloc(vp(16), vp(16), vp(16), cu.ctypes.data_as(vp), vp(16), 1, 4, 16,
-                                    1, ctypes.c_float(0.25), 0, 16_000_000, 4, vp(16), None, None)
+                                    1, ctypes.c_float(0.25), 0, 16_000_000, 4, 0, vp(16), None, None)
     assert rc == K.KPOOL_EWORKSPACE
     msg = K.lib().kpool_last_error().decode()
     assert "static scratch" in msg and "68000000" in msg
     # the other argument checks are those of kpool_score_topk
     cu = np.array([0, 64], dtype=np.int32)
     assert L.kpool_score_topk_noalloc(vp(16), vp(16), vp(16), cu.ctypes.data_as(vp), vp(16), 1, 4, 16,
-                                      4, ctypes.c_float(0.25), 5, 4, 4, vp(16), None, None) == K.KPOOL_EINVAL
+                                      4, ctypes.c_float(0.25), 5, 4, 4, 0, vp(16), None, None) == K.KPOOL_EINVAL
+    assert L.kpool_score_topk_noalloc(vp(16), vp(16), vp(16), cu.ctypes.data_as(vp), vp(16), 1, 4, 16,
+                                      4, ctypes.c_float(0.25), 0, 64, 4, 4, vp(16), None, None) == K.KPOOL_EINVAL
     assert L.kpool_score_topk_noalloc(None, None, None, cu.ctypes.data_as(vp), None, 1, 4, 16, 4,
-                                      ctypes.c_float(0.25), 9, 9, 4, None, None, None) == K.KPOOL_OK
+                                      ctypes.c_float(0.25), 9, 9, 4, 0, None, None, None) == K.KPOOL_OK
