@@ -33,6 +33,8 @@
 //   Arithmetic: bf16 x bf16 products accumulated by the MFMA in fp32; the
 //   epilogue forms relu(dot) * (scale * w[h]) in fp32 (scale > 0, so this is
 //   the same quantity as w * relu(scale * dot)) and sums the heads in fp32.
+#include <type_traits>
+
 #include "kpool_internal.h"
 
 namespace kpool {
@@ -166,8 +168,6 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
       uni_ptr(out), 0, (int)__builtin_amdgcn_readfirstlane(tile_end * (uint32_t)ld * 4u), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_gmax = __builtin_amdgcn_make_buffer_rsrc(
       uni_ptr(gmax), 0, (int)__builtin_amdgcn_readfirstlane(tile_end * (uint32_t)ldg * 4u), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc(
-      uni_ptr(kps), 0, (int)__builtin_amdgcn_readfirstlane((uint32_t)p_end * D * 2u), kRsrcWord3);
 #endif
 
   // ---- pooled-key stages through LDS ---------------------------------------
@@ -180,26 +180,39 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   // scores are finite and never read), and chunks past D (padding of the K step) meet
   // zero q fragments, so duplicates are harmless.
   auto swz = [](int pool) { return (pool >> 2) & (S::NSLOT - 1); };
-  // Lane offsets of the DMA regions are recomputed per stage from the lane id (a few
-  // VALU instructions per stage) rather than held in VGPRs across the loop.
+  // Per-lane byte offsets of the DMA regions inside a stage (a stage starts at a multiple
+  // of 64 pools, so the swizzle of a lane's pool does not depend on the stage), computed
+  // once.  Each stage's loads go through a buffer resource based at the stage's first
+  // pool whose range ends at p_end: loads of pools at or past p_end fall outside it and
+  // are dropped by the hardware range check (their LDS rows then hold zeros or an older
+  // stage's keys; their scores are never stored).
+  uint32_t dma_off[S::RGW];
+#pragma unroll
+  for (int i = 0; i < S::RGW; ++i) {
+    const int byte = (wave + i * kWaves) * 1024 + lane * 16;
+    const int pl = byte / S::ROWB;
+    const int off = min((((byte % S::ROWB) / 16) ^ swz(pl)) * 8, D - 8);
+    dma_off[i] = (uint32_t)(pl * D + off) * 2u;
+  }
+  const int p_begin_u = __builtin_amdgcn_readfirstlane(p_begin);
+  const int p_end_u = __builtin_amdgcn_readfirstlane(p_end);
+  const uint16_t *kps_u = (const uint16_t *)uni_ptr(kps);
   auto dma_stage = [&](int stage_base, int buf) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(kps_u + (int64_t)stage_base * D), 0, (p_end_u - stage_base) * D * 2, kRsrcWord3);
+#endif
 #pragma unroll
     for (int i = 0; i < S::RGW; ++i) {
       if (S::NREG % kWaves == 0 || wave + i * kWaves < S::NREG) {  // wave-uniform
-        const int byte = (wave + i * kWaves) * 1024 + lane * 16;
-        const int pl = byte / S::ROWB;
-        const int off = min((((byte % S::ROWB) / 16) ^ swz(pl)) * 8, D - 8);
-        const int pool = min(stage_base + pl, p_end - 1);
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only emits the launch stub
+#if defined(__HIP_DEVICE_COMPILE__)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs_kp,
+            rs,
             (__attribute__((address_space(3))) void *)(lds + buf * S::STAGE_BYTES +
                                                        (wave + i * kWaves) * 1024),
-            16, (uint32_t)(pool * D + off) * 2u, 0, 0, 0);
+            16, dma_off[i], 0, 0, 0);
 #else
-        (void)pool;
-        (void)off;
-        (void)kps;
+        (void)buf;
 #endif
       }
     }
@@ -223,6 +236,18 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     const int rr = wr0 + 4 * j + lg;
     store_lim[j] = rr < nrows ? min((int)((t0 + rr) / kpool) + 1, p_end) : 0;
   }
+  // Lane-constant parts, so that a stage (base = its first pool, a multiple of 64, the
+  // same for the whole wave) adds one scalar: the lane's pools are base + 4 lc + sub,
+  // visible while sub < lim_rel - base; its score bytes start at so_lane + 4 base and its
+  // group max at go_lane + base / 4 (pool base + 4 lc is in group base / 16 + lc / 4).
+  int lim_rel[kQuads];
+  uint32_t so_lane[kQuads], go_lane[kQuads];
+#pragma unroll
+  for (int j = 0; j < kQuads; ++j) {
+    lim_rel[j] = store_lim[j] - 4 * lc;
+    so_lane[j] = orow_off[j] + 16u * (uint32_t)lc;
+    go_lane[j] = grow_off[j] + 4u * (uint32_t)(lc >> 2);
+  }
   // A stage's reduced scores stay in registers (lane (g, c) holds pools 4c .. 4c + 3 of
   // row g) until its last sub-tile is reduced, then go out with one 16-byte store per
   // lane, so every score row is written in whole 256-byte runs.  A lane stores when its
@@ -238,17 +263,16 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   float vals[kQuads][kSubs] = {};
   // lane-local part of the group max (the lane's 4 pools, over the row's visible pools)
   auto flush_max = [&](int j, int base) {
-    const int p0 = base + 4 * lc;
+    const int d = lim_rel[j] - base;  // this lane's pools base + 4 lc + sub are visible for sub < d
     float m = -__builtin_inff();
 #pragma unroll
-    for (int sub = 0; sub < kSubs; ++sub) m = fmaxf(m, p0 + sub < store_lim[j] ? vals[j][sub] : -__builtin_inff());
+    for (int sub = 0; sub < kSubs; ++sub) m = fmaxf(m, sub < d ? vals[j][sub] : -__builtin_inff());
     return m;
   };
   auto flush_store = [&](int j, int base, bool live, float m) {
-    const int p0 = base + 4 * lc;
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
     m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x4E, 0xF, 0xF, true)));
-    const bool vis = live && p0 < store_lim[j];
+    const bool vis = live && 0 < lim_rel[j] - base;
 #if defined(__HIP_DEVICE_COMPILE__)
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 u = {__float_as_uint(vals[j][0]), __float_as_uint(vals[j][1]),
@@ -257,10 +281,10 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     // them are never read back, so they should not push the group maxima, which the
     // selection reads next, out of the caches.
     constexpr int kNonTemporal = 2;
-    __builtin_amdgcn_raw_buffer_store_b128(u, rs_out, vis ? orow_off[j] + 4u * (uint32_t)p0 : kDrop, 0,
+    __builtin_amdgcn_raw_buffer_store_b128(u, rs_out, vis ? so_lane[j] + 4u * (uint32_t)base : kDrop, 0,
                                            kNonTemporal);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rs_gmax,
-                                          vis && (lc & 3) == 0 ? grow_off[j] + 4u * (uint32_t)(p0 / kSub) : kDrop,
+                                          vis && (lc & 3) == 0 ? go_lane[j] + (uint32_t)base / 4u : kDrop,
                                           0, 0);
 #endif
   };
@@ -298,8 +322,8 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     return *reinterpret_cast<const bf16x8 *>(sb + b_addr(4 * lc + sub, lg * (S::KG / 8) + ks));
   };
 
-  const int nstage = (p_end - p_begin + kStagePools - 1) / kStagePools;
-  dma_stage(p_begin, 0);
+  const int nstage = (p_end_u - p_begin_u + kStagePools - 1) / kStagePools;  // wave-uniform
+  dma_stage(p_begin_u, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first stage's keys have landed
   __syncthreads();
   // Explicit schedule.  Each chain is one scheduling region (a full scheduling barrier
@@ -351,9 +375,12 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     }
     return n;
   };
-  for (int st = 0; st < nstage; ++st) {
-    const int stage_base = p_begin + st * kStagePools;
-    const unsigned char *sb = lds + (st & 1) * S::STAGE_BYTES;
+  // The stage loop is unrolled by two so that the LDS buffer of a stage is a constant:
+  // the B-fragment reads then carry it in their immediate offset.
+  auto stage = [&](int st, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const int stage_base = p_begin_u + st * kStagePools;
+    const unsigned char *sb = lds + BUF * S::STAGE_BYTES;
     // One set of B fragments: the next sub-tile's are read into the same registers
     // right after the last chain's MFMAs of this one (a second set, read a whole
     // sub-tile ahead, measured 0.5% slower and costs 14 VGPRs).
@@ -365,7 +392,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
         const int gp = sub * NCH + c;
         if (gp == 0) {
           // the next stage's key DMA goes out before any of this stage's stores
-          if (st + 1 < nstage) dma_stage(stage_base + kStagePools, (st + 1) & 1);
+          if (st + 1 < nstage) dma_stage(stage_base + kStagePools, BUF ^ 1);
 #pragma unroll
           for (int ks = 0; ks < S::KS; ++ks) b[ks] = b_read(sb, 0, ks);
         }
@@ -404,6 +431,10 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
     static_assert(2 * kQuads < 16, "vmcnt field");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kQuads));  // vmcnt(2 * kQuads), no other counter
     __syncthreads();
+    };
+  for (int st = 0; st < nstage; st += 2) {
+    stage(st, std::integral_constant<int, 0>{});
+    if (st + 1 < nstage) stage(st + 1, std::integral_constant<int, 1>{});
   }
   // drain: the last two chains' epilogues, then the reductions and stores that fall
   // past the last stage
@@ -411,7 +442,7 @@ __global__ __launch_bounds__(kWaves * 64) void score_kernel(
   pb = pa;
   epi(NCH - 1);
   {
-    const int last_base = p_begin + (nstage - 1) * kStagePools;
+    const int last_base = p_begin_u + (nstage - 1) * kStagePools;
 #pragma unroll
     for (int pos = kStageChains; pos < 2 * kStageChains; ++pos) extras(pos, last_base + kStagePools, nstage);
   }
