@@ -1,11 +1,13 @@
 """Benchmark of the k-pool indexer selection on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload sq524288] [--overlap on|off]
-                    [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload sq524288] [--overlap off|on]
+                    [--workspace-mib M] [--no-cpu-baseline]
 
 One step is the whole path (pool the keys, score + select every row through
 the 2 GiB chunk loop, expand to token ids) over the workload's rows, on
-synthetic seeded inputs already resident in HBM.  Prints ONE JSON line:
+synthetic seeded inputs already resident in HBM.  By default one chunk buffer
+holds at most 2 GiB of fp32 scores, the pages' cap, and chunks run one after
+the other on one stream.  Prints ONE JSON line:
 
   value       visible (row, pool) scores per second of whole-path wall time
   ms_per_step selection wall time of one step
@@ -14,9 +16,9 @@ synthetic seeded inputs already resident in HBM.  Prints ONE JSON line:
               the 2.5 PFLOP/s dense bf16 peak.  Launch times come from HIP
               events that the library records around each launch on its
               stream, in a kernel pass of the same K steps run right after the
-              timed region with the chunk overlap off, so that every launch
-              runs alone (overlapped launches share the CUs and their event
-              spans include the other stream's kernels)
+              timed region with every launch alone on one stream (with the
+              chunk overlap on, overlapped launches share the CUs and their
+              event spans would include the other stream's kernels)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same
               workload's rows, extrapolated to the whole job by visible pairs
   probe_peaks what this machine reaches on plain work, measured after the kernel
@@ -219,8 +221,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="sq524288")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--overlap", choices=("on", "off"), default="on",
-                    help="chunk overlap (two buffers on two streams) in the timed region")
+    ap.add_argument("--overlap", choices=("on", "off"), default="off",
+                    help="chunk overlap in the timed region: on = two chunk buffers of up to 2 GiB "
+                         "each on two streams (KPOOL_FLAG_OVERLAP); off (default) = one chunk "
+                         "buffer, so all fp32 scores in flight stay within the 2 GiB cap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--workspace-mib", type=int, default=None,
