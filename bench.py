@@ -323,8 +323,8 @@ def main():
 
     cnt = committed_counters(wl.name)
     chunk_rows = sel.chunk_rows()
-    pitch = ((sel.max_pools + 63) // 64) * 64
-    nbuf = 2 if overlap and sel.workspace_bytes >= 2 * (pitch + pitch // 16) * 4 else 1
+    nbuf = sel.chunk_buffers()
+    pitch = ((sel.max_pools + 63) // 64) * 64    # (the fp32 score row pitch, for the byte counts)
     score_launch_ms = score_ms / max(1, score_n)
     topk_launch_ms = topk_ms / max(1, topk_n)
     topk = {"ms_per_step": topk_ms / S, "launches_per_step": topk_n // S,

@@ -135,6 +135,15 @@ size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools, int3
 /* Flags of kpool_score_topk. */
 #define KPOOL_FLAG_OVERLAP 1u /* two chunk buffers, chunks alternating between two streams */
 
+/* The chunk plan kpool_score_topk follows for a sequence of at most max_pools pools
+ * (per kpool_count_pools with the same tail flag), a workspace of workspace_bytes and
+ * these flags: returns the rows per chunk (> 0; each chunk's fp32 scores at most
+ * 2 GiB) and writes the number of chunk buffers (1, or 2 with KPOOL_FLAG_OVERLAP and
+ * room for two rows) to *nbuf_out (nullable).  Returns a negative kpool_status for
+ * max_pools < 1, unknown flags, or a workspace smaller than one row. */
+int64_t kpool_chunk_rows(int32_t max_pools, size_t workspace_bytes, uint32_t flags,
+                         int32_t *nbuf_out);
+
 /* Step 2 - score and select, for the global rows [q_lo, q_hi).
  * (Megatron-LM PR #8299 "Change": one rank's contiguous slice of query rows
  * goes through the chunked score/top-k path; per row the result equals the

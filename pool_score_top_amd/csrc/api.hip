@@ -172,6 +172,20 @@ hipError_t scratch_ptr(hipStream_t stream, void **out) {
 
 // Per row of a chunk the workspace holds ld fp32 scores and ld/16 fp32 group maxima.
 int64_t ws_row_bytes(int64_t ld) { return (ld + ld / kpool::kGroup) * 4; }
+
+// The chunk plan of the loop: the number of chunk buffers and the rows per chunk for a
+// score pitch ld and a workspace of the given size (at least one row).
+struct ChunkPlan {
+  int nbuf;
+  int64_t rows;
+};
+ChunkPlan plan_chunks(int64_t ld, size_t workspace_bytes, bool overlap) {
+  const int64_t row_bytes = ws_row_bytes(ld);
+  const int nbuf = (overlap && (int64_t)workspace_bytes >= 2 * row_bytes) ? 2 : 1;
+  const int64_t rows = std::max<int64_t>(
+      1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / nbuf / row_bytes));
+  return {nbuf, rows};
+}
 // The chunk loop behind kpool_score_topk and kpool_score_topk_noalloc.  With
 // use_scratch, the workspace is this device's static scratch array (resolved after the
 // arguments are validated), chunks run on the caller's stream one after the other and
@@ -246,9 +260,9 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
   // chunks then alternate between the caller's stream and a helper stream, so one
   // chunk's selection and the next chunk's scoring overlap instead of draining the GPU
   // between launches.  Each buffer's fp32 score rows stay within the 2 GiB cap.
-  const int nbuf = ((flags & KPOOL_FLAG_OVERLAP) && (int64_t)workspace_bytes >= 2 * row_bytes) ? 2 : 1;
-  const int64_t chunk_rows = std::max<int64_t>(
-      1, std::min<int64_t>(kChunkCapBytes / (ld * 4), (int64_t)workspace_bytes / nbuf / row_bytes));
+  const ChunkPlan plan = plan_chunks(ld, workspace_bytes, flags & KPOOL_FLAG_OVERLAP);
+  const int nbuf = plan.nbuf;
+  const int64_t chunk_rows = plan.rows;
   const int64_t nchunks = (q_hi - q_lo + chunk_rows - 1) / chunk_rows;
   float *ws_buf[2], *gws_buf[2];
   for (int b = 0; b < 2; ++b) {
@@ -402,6 +416,20 @@ size_t kpool_workspace_bytes(int64_t q_lo, int64_t q_hi, int32_t max_pools, int3
   const int64_t cap_rows = std::max<int64_t>(1, kChunkCapBytes / (ld * 4));
   // nbuf full chunk buffers when the rows need more than one chunk
   return (size_t)(std::min<int64_t>(q_hi - q_lo, nbuf * cap_rows) * ws_row_bytes(ld));
+}
+
+int64_t kpool_chunk_rows(int32_t max_pools, size_t workspace_bytes, uint32_t flags,
+                         int32_t *nbuf_out) {
+  if (max_pools <= 0) return fail(KPOOL_EINVAL, "kpool_chunk_rows: max_pools must be >= 1");
+  if (flags & ~(uint32_t)(KPOOL_FLAG_OVERLAP | KPOOL_FLAG_TAIL))
+    return fail(KPOOL_EINVAL, "kpool_chunk_rows: unknown flags 0x%x", flags);
+  const int64_t ld = pitch_of(max_pools);
+  if ((int64_t)workspace_bytes < ws_row_bytes(ld))
+    return fail(KPOOL_EWORKSPACE, "kpool_chunk_rows: workspace smaller than one score row");
+  const ChunkPlan plan = plan_chunks(ld, workspace_bytes, flags & KPOOL_FLAG_OVERLAP);
+  if (nbuf_out) *nbuf_out = plan.nbuf;
+  ok();
+  return plan.rows;
 }
 
 int kpool_score_topk(const uint16_t *q, const uint16_t *kp, const float *w,

@@ -47,6 +47,7 @@ def lib():
         "kpool_pool_keys": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, u32, vp, vp]),
         "kpool_pool_keys_gated": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, i32, u32, vp, vp]),
         "kpool_workspace_bytes": (sz, [i64, i64, i32, i32]),
+        "kpool_chunk_rows": (i64, [i32, sz, u32, vp]),
         "kpool_score_topk": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i64, i64,
                                             i32, vp, sz, u32, vp, vp, vp]),
         "kpool_score_topk_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
@@ -135,6 +136,15 @@ def workspace_bytes(q_lo: int, q_hi: int, max_pools: int, nbuf: int = 2) -> int:
     """Workspace of score_topk over rows [q_lo, q_hi): nbuf chunk buffers (2 for the
     chunk overlap, 1 without), each capped at 2 GiB of fp32 scores."""
     return int(lib().kpool_workspace_bytes(q_lo, q_hi, max_pools, nbuf))
+
+
+def chunk_rows(max_pools: int, workspace_bytes: int, overlap: bool = False, tail: bool = False):
+    """(rows per chunk, chunk buffers) of score_topk's chunk loop for this workspace."""
+    nbuf = ctypes.c_int32(0)
+    rows = lib().kpool_chunk_rows(max_pools, workspace_bytes,
+                                  (KPOOL_FLAG_OVERLAP if overlap else 0) | _tail(tail), ctypes.byref(nbuf))
+    _check(0 if rows >= 0 else rows, "kpool_chunk_rows")
+    return int(rows), int(nbuf.value)
 
 
 def pool_keys(k, cu_seqlens, cu_seqlens_dev, cu_pools_dev, kpool: int, out=None, stream=None,
@@ -323,12 +333,13 @@ class Selector:
         return self.workspace.numel()
 
     def chunk_rows(self, overlap: bool | None = None) -> int:
-        """Rows per chunk of the chunk loop with this workspace (as the library plans it)."""
+        """Rows per chunk of the chunk loop with this workspace (the library's plan)."""
         overlap = self.overlap if overlap is None else overlap
-        ld = (self.max_pools + 63) // 64 * 64
-        row_bytes = (ld + ld // 16) * 4
-        nbuf = 2 if overlap and self.workspace_bytes >= 2 * row_bytes else 1
-        return max(1, min((1 << 31) // (ld * 4), self.workspace_bytes // nbuf // row_bytes))
+        return chunk_rows(self.max_pools, self.workspace_bytes, overlap, self.tail)[0]
+
+    def chunk_buffers(self, overlap: bool | None = None) -> int:
+        overlap = self.overlap if overlap is None else overlap
+        return chunk_rows(self.max_pools, self.workspace_bytes, overlap, self.tail)[1]
 
     def run(self, q, k, w, scores_out=None, stream=None, overlap: bool | None = None, g=None,
             ape=None):

@@ -60,6 +60,35 @@ def test_count_pools_and_workspace():
     assert K.workspace_bytes(0, 3, 1, 0) == 0 and K.workspace_bytes(0, 3, 1, 3) == 0
 
 
+@pytest.mark.parametrize("max_pools", [1, 63, 64, 65, 7000, 131072, 262144])
+@pytest.mark.parametrize("ws", [272, 4 << 20, 1 << 31, (1 << 32) + 12345, 40 << 30])
+@pytest.mark.parametrize("overlap", [False, True])
+def test_chunk_plan_properties(max_pools, ws, overlap):
+    """The chunk plan: whole 64-float score rows plus one group maximum per 16 pools,
+    each chunk's fp32 scores within 2 GiB, all chunk buffers within the workspace, and
+    no room for one more row under either limit."""
+    pitch = (max_pools + 63) // 64 * 64
+    row = (pitch + pitch // 16) * 4
+    if ws < row:
+        with pytest.raises(K.KpoolError):
+            K.chunk_rows(max_pools, ws, overlap)
+        return
+    rows, nbuf = K.chunk_rows(max_pools, ws, overlap)
+    assert nbuf == (2 if overlap and ws >= 2 * row else 1)
+    assert rows >= 1 and rows * pitch * 4 <= 1 << 31 and nbuf * rows * row <= ws
+    assert (rows + 1) * pitch * 4 > 1 << 31 or nbuf * (rows + 1) * row > ws
+    # the tail flag does not change the plan for the same pool count
+    assert K.chunk_rows(max_pools, ws, overlap, tail=True) == (rows, nbuf)
+
+
+def test_chunk_plan_rejects():
+    L = K.lib()
+    assert L.kpool_chunk_rows(0, 1 << 20, 0, None) == K.KPOOL_EINVAL
+    assert L.kpool_chunk_rows(10, 1 << 20, 4, None) == K.KPOOL_EINVAL
+    assert L.kpool_chunk_rows(10, 271, 0, None) == K.KPOOL_EWORKSPACE
+    assert L.kpool_chunk_rows(10, 272, 0, None) == 1
+
+
 def _call_score(**kw):
     L = K.lib()
     cu = np.array(kw.pop("cu", [0, 64]), dtype=np.int32)
