@@ -85,12 +85,6 @@ __device__ inline uint64_t raw_to_key(uint64_t r) {
   return ((uint64_t)order_key(__uint_as_float((uint32_t)(r >> 32))) << 32) | (r & 0xFFFFFFFFull);
 }
 
-__device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  const uint32_t lo = __shfl_xor((unsigned)(uint32_t)v, mask);
-  const uint32_t hi = __shfl_xor((unsigned)(uint32_t)(v >> 32), mask);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // The float whose order key is k, for k = 0 (a NaN) or a key of a non-NaN value
 // (k >= order_key(-inf)); with it, order_key(x) >= k reads as x >= key_float(k)
 // for every non-NaN x when k != 0, and NaN (key 0) never passes.
@@ -117,6 +111,45 @@ __device__ inline uint32_t wave_kth_desc(const uint32_t (&x)[NMAX], int rank) {
     else r -= cnt;
   }
   return prefix;
+}
+
+// The value of lane (lane ^ D), D a power of two below 64, with D known at compile
+// time: quad permutations for 1 and 2 (DPP), a fixed-pattern swizzle within 32 lanes for
+// 4 to 16, and for 32 the half-wave swap (permlane32_swap(x, x) gives [x.lo, x.lo] and
+// [x.hi, x.hi]).  No lane address is computed, and a stage's exchanges of all its keys
+// are issued before the first is waited for.  (Measured against a generic lane
+// permute: the selection is 2.4% faster at budget 512 and 5% at budget 2048; DPP or the
+// 16-lane swap for distances 8 and 16, or swizzles for 1 and 2, were slower.)
+template <int D>
+__device__ inline uint32_t lanes_xor(uint32_t x) {
+  if constexpr (D == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+  else if constexpr (D == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+  else if constexpr (D < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (D << 10));
+  else {
+    const auto z = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (__lane_id() & 32) ? z[0] : z[1];
+  }
+}
+template <int D>
+__device__ inline uint64_t lanes_xor_u64(uint64_t v) {
+  return ((uint64_t)lanes_xor<D>((uint32_t)(v >> 32)) << 32) | lanes_xor<D>((uint32_t)v);
+}
+// The compare-exchange stages of one bitonic merge step k at lane distances D, D/2, ..
+// 1 (distance j = D*M keys, those with j <= k/2).
+template <int D, int M>
+__device__ inline void lane_stages(uint64_t (&v)[M], int k, int tid, int e0) {
+  if constexpr (D >= 1) {
+    if (D * M <= (k >> 1)) {
+      const bool lower = (tid & D) == 0;
+      const bool desc = (e0 & k) == 0;
+      uint64_t p[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) p[m] = lanes_xor_u64<D>(v[m]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[m] = ((p[m] > v[m]) == (lower == desc)) ? p[m] : v[m];
+    }
+    lane_stages<D / 2, M>(v, k, tid, e0);
+  }
 }
 
 // Bitonic sort (descending) of kThreads*M keys in a blocked layout: thread t holds
@@ -147,18 +180,8 @@ __device__ void block_sort_desc(uint64_t (&v)[M], uint64_t *buf, int tid) {
         v[m] = ((p > v[m]) == (lower == desc)) ? p : v[m];  // larger kept when lower == desc
       }
     }
-    // distances across lanes of one wave
-#pragma unroll 1
-    for (int j = min(k >> 1, 32 * M); j >= M; j >>= 1) {
-      const int d = j / M;
-      const bool lower = (tid & d) == 0;
-      const bool desc = (e0 & k) == 0;
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const uint64_t p = shfl_xor_u64(v[m], d);
-        v[m] = ((p > v[m]) == (lower == desc)) ? p : v[m];  // larger kept when lower == desc
-      }
-    }
+    // distances across lanes of one wave (larger kept when lower == desc)
+    lane_stages<32, M>(v, k, tid, e0);
     // distances inside a thread
 #pragma unroll
     for (int j = M / 2; j > 0; j >>= 1) {
