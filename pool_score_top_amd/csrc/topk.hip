@@ -253,7 +253,7 @@ __device__ inline uint32_t wave_reserve(uint32_t c, uint32_t *counter, int lane)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)b[i], 0u)) << i;
   uint32_t base = 0;
   if (lane == 0) base = atomicAdd(counter, tot);
-  return __shfl(base, 0) + pre;
+  return __builtin_amdgcn_readfirstlane(base) + pre;  // every lane is active here
 }
 
 // One radix-select step, run by one whole wave: hist holds the 256 counts of the next
@@ -269,11 +269,19 @@ __device__ inline void next_digit(SM &sm, uint64_t prefix, int pbits, int krem, 
     c[i] = sm.hist[255 - 4 * lane - i];
     tot += c[i];
   }
-  uint32_t incl = tot;  // inclusive prefix over lanes, i.e. over digits from the top
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+  // inclusive prefix over lanes, i.e. over digits from the top: within each 16-lane row
+  // by shifted adds (DPP row_shr, lanes shifted in from outside the row read 0), then the
+  // totals of the rows before
+  uint32_t incl = tot;
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x111, 0xF, 0xF, false);  // row_shr:1
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x112, 0xF, 0xF, false);  // row_shr:2
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x114, 0xF, 0xF, false);  // row_shr:4
+  incl += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x118, 0xF, 0xF, false);  // row_shr:8
+  {
+    const uint32_t r0 = __builtin_amdgcn_readlane(incl, 15), r1 = __builtin_amdgcn_readlane(incl, 31),
+                   r2 = __builtin_amdgcn_readlane(incl, 47);
+    const int row = lane >> 4;
+    incl += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
   }
   const uint32_t excl = incl - tot;
   // the digits hold at least krem keys in all, so some lane reaches it
@@ -429,8 +437,13 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
     }
     const int rank = (budget + kWavesT - 1) / kWavesT;  // 1..64*NMAX
     const uint32_t wb = wave_kth_desc<NMAX>(tmax, rank);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lm = max(lm, (uint32_t)__shfl_xor((int)lm, o));
+    // the wave's best key: a butterfly over compile-time lane distances
+    lm = max(lm, lanes_xor<32>(lm));
+    lm = max(lm, lanes_xor<16>(lm));
+    lm = max(lm, lanes_xor<8>(lm));
+    lm = max(lm, lanes_xor<4>(lm));
+    lm = max(lm, lanes_xor<2>(lm));
+    lm = max(lm, lanes_xor<1>(lm));
     if (lane == 0) {
       sm.wave_bound[wave] = wb;
       sm.wave_max[wave] = lm;
