@@ -82,11 +82,14 @@ hipError_t timed(int kind, hipStream_t stream, F &&launch) {
   hipError_t e = hipEventCreate(&rec.a);
   if (e == hipSuccess) e = hipEventCreate(&rec.b);
   if (e == hipSuccess) e = hipEventRecord(rec.a, stream);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(rec.b, stream);
-  if (e == hipSuccess) g_prof.push_back(rec);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(rec.b, stream);
+  if (e == hipSuccess) {
+    g_prof.push_back(rec);
+  } else {  // (the launch's own error is returned; the record is dropped)
+    if (rec.a) (void)hipEventDestroy(rec.a);
+    if (rec.b) (void)hipEventDestroy(rec.b);
+  }
   return e;
 }
 
@@ -123,12 +126,21 @@ hipError_t get_aux(hipStream_t stream, Aux **out) {
     std::unique_ptr<Aux> a(new Aux);
     int cur = 0;
     e = hipGetDevice(&cur);
-    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    const bool switched = e == hipSuccess && cur != dev;
+    if (switched) e = hipSetDevice(dev);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&a->helper, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&a->join, hipEventDisableTiming);
-    if (cur != dev) (void)hipSetDevice(cur);
-    if (e != hipSuccess) return e;  // (a partly made helper is dropped; the next call retries)
+    if (e != hipSuccess) {  // a partly made helper is released; the next call retries
+      if (a->join) (void)hipEventDestroy(a->join);
+      if (a->fork) (void)hipEventDestroy(a->fork);
+      if (a->helper) (void)hipStreamDestroy(a->helper);
+    }
+    if (switched) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      g_aux.erase({dev, stream});
+      return e;
+    }
     slot = std::move(a);
   }
   *out = slot.get();
@@ -159,10 +171,11 @@ hipError_t scratch_ptr(hipStream_t stream, void **out) {
   if (!g_scratch_ptr[dev]) {
     int cur = 0;
     e = hipGetDevice(&cur);
-    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    const bool switched = e == hipSuccess && cur != dev;
+    if (switched) e = hipSetDevice(dev);
     void *p = nullptr;
     if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (cur != dev) (void)hipSetDevice(cur);
+    if (switched) (void)hipSetDevice(cur);
     if (e != hipSuccess) return e;
     g_scratch_ptr[dev] = p;
   }
