@@ -283,6 +283,13 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
     gws_buf[b] = ws_buf[b] + chunk_rows * ld;  // group maxima follow the score rows
   }
   const int tile_rows = kpool::score_tile_rows();
+  // score workgroups the device runs at once, for the segment plan below (0: unknown)
+  int slots = 0;
+  {
+    int dev = 0;
+    if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) == hipSuccess)
+      slots = kpool::score_slots(H, D, dev);
+  }
 
   // score + select of rows [c0, c1) into one buffer, on one stream
   auto enqueue_chunk = [&](int64_t c0, int64_t c1, float *ws, float *gws, hipStream_t cs) -> hipError_t {
@@ -314,12 +321,32 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
         max_npv = std::max<int32_t>(max_npv, std::min((sg.hi - 1 - sg.start) / kpool + 1, sg.pool_count));
       }
       L.tile_start[L.nseg] = ntiles;
-      // pool segments per tile: about KPOOL_SCORE_TARGET_WGS workgroups per launch (4 per
-      // CU), at most kPoolSegMax pools each; fewer, longer workgroups reload q less often
+      // Pool segments per tile: at most KPOOL_SCORE_TARGET_WGS workgroups per launch (4 per
+      // CU), segments of 64..kPoolSegMax pools; fewer, longer workgroups reload q less
+      // often.  Among the segment counts from that target down to the fewest the size cap
+      // allows, take the one whose rounds of workgroups over the device's slots, each as
+      // long as one segment, cover the tiles soonest: a last round that is nearly empty
+      // costs a whole segment's time.  Ties keep more segments.
+      auto seg_pools = [&](int64_t ns) {
+        const int64_t ps = (max_npv + ns - 1) / ns;
+        return std::min<int64_t>(kPoolSegMax, std::max<int64_t>(64, (ps + 63) / 64 * 64));
+      };
       const int64_t want_segs =
           std::max<int64_t>(1, (KPOOL_SCORE_TARGET_WGS + ntiles - 1) / ntiles);
-      int64_t pseg = (max_npv + want_segs - 1) / want_segs;
-      pseg = std::min<int64_t>(kPoolSegMax, std::max<int64_t>(64, (pseg + 63) / 64 * 64));
+      const int64_t min_segs = std::max<int64_t>(1, (max_npv + kPoolSegMax - 1) / kPoolSegMax);
+      int64_t pseg = seg_pools(want_segs);
+      if (slots > 0) {
+        int64_t best = -1;
+        for (int64_t ns = std::max(want_segs, min_segs); ns >= min_segs; --ns) {
+          const int64_t ps = seg_pools(ns);
+          const int64_t nwg = (int64_t)ntiles * ((max_npv + ps - 1) / ps);
+          const int64_t cost = (nwg + slots - 1) / slots * ps;
+          if (best < 0 || cost < best) {
+            best = cost;
+            pseg = ps;
+          }
+        }
+      }
       const int32_t npseg = (int32_t)((max_npv + pseg - 1) / pseg);
       hipError_t e = timed_if(!use_scratch, 1, cs, [&] {
         return kpool::launch_score(H, D, q, kp, w, scale, kpool, L, ntiles, npseg, (int32_t)pseg,

@@ -41,6 +41,8 @@ hipError_t launch_pool_keys_gated(const uint16_t *k, const uint16_t *g, const fl
 // true if (H, D) has a compiled score kernel
 bool score_supported(int H, int D);
 int score_tile_rows();
+// Score workgroups the device runs at once (CUs x workgroups per CU), 0 if unknown.
+int score_slots(int H, int D, int device);
 // Scores of the chunk's rows go to out[(row - chunk_row0) * ld + pool]; the max of each
 // 16-pool group of a row (over its visible pools) to gmax[(row - chunk_row0) * ldg + pool/16].
 constexpr int kGroup = 16;

@@ -33,6 +33,7 @@
 //   Arithmetic: bf16 x bf16 products accumulated by the MFMA in fp32; the
 //   epilogue forms relu(dot) * (scale * w[h]) in fp32 (scale > 0, so this is
 //   the same quantity as w * relu(scale * dot)) and sums the heads in fp32.
+#include <atomic>
 #include <type_traits>
 
 #include "kpool_internal.h"
@@ -475,6 +476,32 @@ hipError_t launch_t(const uint16_t *q, const uint16_t *kp, const float *w, float
 
 bool score_supported(int H, int D) { return (H == 32 && D == 128) || (H == 4 && D == 16); }
 int score_tile_rows() { return kTileRows; }
+
+int score_slots(int H, int D, int device) {
+  // (cached per device and shape; the query runs with the caller's current device, which
+  // the library's entry points leave as the stream's device)
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs][2];
+  const int shape = (H == 32 && D == 128) ? 0 : 1;
+  if (device >= 0 && device < kDevs) {
+    const int c = cache[device][shape].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) {
+    if (shape == 0)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<32, 128>, kWaves * 64,
+                                                       2 * Shape<32, 128>::STAGE_BYTES);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_kernel<4, 16>, kWaves * 64,
+                                                       2 * Shape<4, 16>::STAGE_BYTES);
+  }
+  if (e != hipSuccess || cus <= 0 || per_cu <= 0) return 0;
+  const int slots = cus * per_cu;
+  if (device >= 0 && device < kDevs) cache[device][shape].store(slots, std::memory_order_relaxed);
+  return slots;
+}
 
 hipError_t launch_score(int H, int D, const uint16_t *q, const uint16_t *kp, const float *w,
                         float scale, int32_t kpool, const SegList &segs, int32_t ntiles,
