@@ -246,7 +246,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the selection would "
+        print("bench.py measures one GPU: this library has no multi-GPU path (the selection would "
               "shard by query rows with one int32 all-gather; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

@@ -30,7 +30,7 @@ Steps, in the order the pages describe the selection op:
                     named but not defined on the pages: this reading's parity
                     against the pages' own operator is unpinned
 
-Sources (the pages this build works from):
+Sources (the pages this oracle follows):
   * Atlas inference docs, ``spark_model/layers/glm5next_dsa/tp.rs``, module
     doc "Why the indexer is REPLICATED, not sharded": the per-head score is a
     weighted ReLU of a scaled dot product summed over heads; pools are
@@ -128,7 +128,7 @@ def pool_keys(k_bits, cu_seqlens, kpool: int, tail: bool = False) -> np.ndarray:
         kp  = bf16_rne(fp32(acc / n_p)).
     Megatron-LM PR #8299 "Mechanism" (rows score the pooled keys); Atlas
     tp.rs module doc (pools of kpool consecutive tokens).  Mean with fp32
-    accumulation and a bf16 result is the reading this build adopts.  With
+    accumulation and a bf16 result is the reading adopted here.  With
     tail=True only the full pools exist (count_pools).
     """
     k = bf16_to_f32(k_bits)
@@ -261,7 +261,7 @@ def row_scores(q_rows_bits, w_rows, kp_bits, cu_pools, seq, t, kpool: int,
     S[i,p] = sum_h w[i,h] * max(0, scale * sum_d q[i,h,d] * kp[s,p,d])
     for p < visible_pools(t) (capped at the sequence's pool count, which
     cu_pools gives; only tail mode's count can be below it).  Atlas tp.rs module doc (the head-weighted
-    ReLU sum); the scale 1/sqrt(D) is this build's reading.  Order of
+    ReLU sum); the scale 1/sqrt(D) is the reading adopted here.  Order of
     operations: dot, times scale, ReLU, times w, sum over heads.
     q_rows_bits: bf16 bits [r, H, D]; w_rows: fp32 [r, H]; kp_bits: [P_tot, D].
     """
