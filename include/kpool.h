@@ -39,7 +39,10 @@
  *     stream (default priority) with two events, created on first use and kept
  *     until the process ends; the helper joins back into the caller's stream
  *     before the call returns, so results are ordered on the caller's stream as
- *     usual.  Calls on different caller streams use different helpers.  The
+ *     usual.  Calls on different caller streams use different helpers.  Besides
+ *     that, per device and once: the number of score workgroups the device runs
+ *     at once (an occupancy query, used to plan launches) and, for
+ *     kpool_score_topk_noalloc, its static scratch array's device address.  The
  *     optional profiler below is per host thread.
  */
 #ifndef KPOOL_H
