@@ -1,7 +1,7 @@
 """Benchmark of the k-pool indexer selection on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload sq524288] [--overlap off|on]
-                    [--workspace-mib M] [--no-cpu-baseline]
+                    [--kpool K] [--budget B] [--workspace-mib M] [--no-cpu-baseline]
 
 One step is the whole path (pool the keys, score + select every row through
 the 2 GiB chunk loop, expand to token ids) over the workload's rows, on
@@ -221,6 +221,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="sq524288")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kpool", type=int, default=None,
+                    help="override the workload's pool size (the workload is then named "
+                         "<workload>_kpool<K>_budget<B>)")
+    ap.add_argument("--budget", type=int, default=None,
+                    help="override the workload's pools kept per row (1..2048)")
     ap.add_argument("--overlap", choices=("on", "off"), default="off",
                     help="chunk overlap in the timed region: on = two chunk buffers of up to 2 GiB "
                          "each on two streams (KPOOL_FLAG_OVERLAP); off (default) = one chunk "
@@ -255,7 +260,11 @@ def main():
     from pool_score_top_amd import kpool as K
     from pool_score_top_amd import synth
 
-    wl = synth.workload(args.workload)
+    over = {k: v for k, v in (("kpool", args.kpool), ("budget", args.budget)) if v is not None}
+    wl = synth.workload(args.workload, **over)
+    if over:
+        wl = synth.Workload(**{**wl.__dict__,
+                               "name": f"{args.workload}_kpool{wl.kpool}_budget{wl.budget}"})
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] generating {wl.name} inputs (T={wl.T}, H={wl.H}, D={wl.D})")

@@ -13,8 +13,9 @@
 //
 // HBM-bound: workgroups stride over rows (one sequence lookup per row), threads over
 // a row's slots.  kpool == 4: each slot is one 16-byte store; kpool == 1 with 16-byte
-// aligned rows: 4 slots per thread through 16-byte loads and stores; otherwise one
-// token per thread and iteration.
+// aligned rows: 4 slots per thread through 16-byte loads and stores; any other kpool
+// whose rows hold a multiple of 4 slots (16-byte aligned output): 4 consecutive slots
+// per thread and one 16-byte store; otherwise one token per thread and iteration.
 #include "kpool_internal.h"
 
 namespace kpool {
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(const int32_t *_
                                                                 const int32_t *__restrict__ cu_seqlens,
                                                                 int nseq, int kpool, bool tail,
                                                                 int64_t q_lo, int64_t nrows,
-                                                                int budget, bool vec,
+                                                                int budget, bool vec, bool vec4,
                                                                 int32_t *__restrict__ tok) {
   const int ntail = tail ? kpool - 1 : 0;
   const int64_t width = (int64_t)budget * kpool + ntail;
@@ -77,6 +78,22 @@ __global__ __launch_bounds__(kExpandThreads) void expand_kernel(const int32_t *_
         const i32x4 o = {f(p.x), f(p.y), f(p.z), f(p.w)};
         __builtin_nontemporal_store(o, reinterpret_cast<i32x4 *>(orow) + j);
       }
+    } else if (vec4) {
+      // any other kpool with rows of a multiple of 4 slots: 4 consecutive slots per thread
+      // (slot e holds token (e / kpool) * kpool-th pool's e % kpool), one 16-byte store
+      const int64_t n4 = (int64_t)budget * kpool / 4;
+      for (int64_t e4 = threadIdx.x; e4 < n4; e4 += kExpandThreads) {
+        int32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = 4 * e4 + k;
+          const int32_t p = prow[e / kpool];
+          const int64_t tk = (int64_t)p * kpool + e % kpool;
+          v[k] = (p >= 0 && tk <= t) ? (int32_t)tk : -1;
+        }
+        const i32x4 o = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<i32x4 *>(orow) + e4);
+      }
     } else {
       const int64_t n = (int64_t)budget * kpool;
       for (int64_t e = threadIdx.x; e < n; e += kExpandThreads) {
@@ -95,9 +112,11 @@ hipError_t launch_expand(const int32_t *pool_ids, const int32_t *cu_seqlens, int
                          int32_t *token_ids, hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
   const bool vec = budget % 4 == 0 && ((uintptr_t)pool_ids % 16) == 0 && ((uintptr_t)token_ids % 16) == 0;
+  // rows of budget * kpool slots start 16-byte aligned when that count is a multiple of 4
+  const bool vec4 = ((int64_t)budget * kpool) % 4 == 0 && ((uintptr_t)token_ids % 16) == 0;
   const unsigned blocks = (unsigned)(nrows < kExpandMaxBlocks ? nrows : kExpandMaxBlocks);
   hipLaunchKernelGGL(expand_kernel, dim3(blocks), dim3(kExpandThreads), 0, stream, pool_ids,
-                     cu_seqlens, nseq, kpool, tail, q_lo, nrows, budget, vec, token_ids);
+                     cu_seqlens, nseq, kpool, tail, q_lo, nrows, budget, vec, vec4, token_ids);
   return hipGetLastError();
 }
 
