@@ -8,9 +8,9 @@
 // Each element is ranked by the 64-bit key (order_key(score) << 32 | ~index):
 // a larger key is better, and keys are unique, so "the best `budget` keys" is
 // exactly the selection.  One workgroup owns one row, and several of them share
-// a CU, so their memory latencies overlap.  Two instances: 256 threads with
-// NMAX = 4 maxima per thread for budgets up to 512, 512 threads with NMAX = 8 up
-// to 2048.
+// a CU, so their memory latencies overlap.  Three instances, by budget: 256
+// threads with NMAX = 4 maxima per thread up to 512, 512 threads with NMAX = 4 up
+// to 1024, and 512 threads with NMAX = 8 up to 2048.
 //
 //   pass 1  (HBM)   every thread keeps NMAX maxima over disjoint parts of its
 //                   elements (or, for long rows, of its 16-pool group maxima,
@@ -37,6 +37,8 @@
 //                   elements, which are then sorted the same way.
 // Rows with no more than `budget` elements skip the bound and keep them all;
 // unused output slots are -1.
+#include <type_traits>
+
 #include "kpool_internal.h"
 
 namespace kpool {
@@ -44,28 +46,49 @@ namespace {
 
 constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // order_key(-inf)
 
-// Two instances, by the number of maxima per thread (NMAX):
-//   NMAX 4: 256 threads, 1024 maxima, budgets up to 512;
-//   NMAX 8: 512 threads, 4096 maxima, budgets up to 2048.
-// Either way a wave's bound is at most its median maximum, so at most about ln 2 x
+// Three instances, by budget:
+//   small   budgets up to 512:   256 threads, NMAX 4 (1024 maxima), lists of 1280;
+//   medium  budgets up to 1024:  512 threads, NMAX 4 (2048 maxima), lists of 2560;
+//   large   budgets up to 2048:  512 threads, NMAX 8 (4096 maxima), lists of 4096.
+// Each way a wave's bound is at most its median maximum, so at most about ln 2 x
 // (number of maxima) candidates are expected, plus the spread of the minimum over
 // waves (iid rows of 16k-131k pools at budget 512: about 775 candidates in about 740
 // groups, at most 930 and 880 over 200 rows).  The top-k is latency-bound, so the
-// small instance is sized for rows in flight: lists of 1280 candidates and 1280
-// groups (16.4 KB of LDS) and rounds of 8 group maxima or 4 score pieces per thread
-// (52 VGPRs) let eight rows share a CU, the limit of eight waves per SIMD.  The large
-// instance holds 4096 of each.  A row
-// that overflows a list takes the exact path, so the caps bound speed, not results.
-template <int NMAX>
+// instances are sized for rows in flight: the small one's lists (16.4 KB of LDS) and
+// rounds of 8 group maxima or 4 score pieces per thread (52 VGPRs) let eight rows
+// share a CU, the limit of eight waves per SIMD; the medium one's (31 KB) four rows of
+// 8 waves; the large one's (49 KB) three.  (Before the medium instance, budgets
+// 513-1024 ran on the large one: 27.3 vs 19.3 ms of top-k per 512k step at budget
+// 1024.)  A row that overflows a list takes the exact path, so the caps bound speed,
+// not results.
+template <int I>
+struct Inst;
+// small: budgets up to 512
+template <>
+struct Inst<0> {
+  static constexpr int kNmax = 4, kThreads = 256, kCand = 1280, kMaxBudget = 512;
+};
+// medium: budgets 513 .. 1024
+template <>
+struct Inst<1> {
+  static constexpr int kNmax = 4, kThreads = 512, kCand = 2560, kMaxBudget = 1024;
+};
+// large: budgets 1025 .. 2048
+template <>
+struct Inst<2> {
+  static constexpr int kNmax = 8, kThreads = 512, kCand = 4096, kMaxBudget = kTopkMaxBudget;
+};
+template <int I>
 struct Cfg {
-  static_assert(NMAX == 4 || NMAX == 8, "maxima per thread");
-  static constexpr int kThreads = NMAX == 4 ? 256 : 512;
+  static constexpr int kNmax = Inst<I>::kNmax;
+  static constexpr int kThreads = Inst<I>::kThreads;
   static constexpr int kWaves = kThreads / 64;
   static constexpr int kRound = 8;   // group maxima per thread per round
   static constexpr int kPieces = 4;  // 16-byte score pieces per thread per round
-  static constexpr int kCand = NMAX == 4 ? 5 * kThreads : 8 * kThreads;  // candidate keys in LDS
-  static constexpr int kGroups = kCand;                                  // candidate 16-pool groups
-  static constexpr int kMaxBudget = NMAX == 4 ? 512 : kTopkMaxBudget;
+  static constexpr int kCand = Inst<I>::kCand;   // candidate keys in LDS
+  static constexpr int kGroups = kCand;          // candidate 16-pool groups
+  static constexpr int kMaxBudget = Inst<I>::kMaxBudget;
+  static_assert(kNmax == 4 || kNmax == 8, "maxima per thread");
   // the cut gathers `budget` keys into the group list's space
   static_assert(kGroups / 2 >= kMaxBudget, "cut buffer");
   // a list longer than the budget's sort size is cut first, so sorts span at most
@@ -218,13 +241,13 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
   }
 }
 
-template <int NMAX>
+template <int I>
 struct Smem {
-  uint64_t cand[Cfg<NMAX>::kCand];
-  uint32_t glist[Cfg<NMAX>::kGroups];
+  uint64_t cand[Cfg<I>::kCand];
+  uint32_t glist[Cfg<I>::kGroups];
   uint32_t hist[256];
-  uint32_t wave_bound[Cfg<NMAX>::kWaves];
-  uint32_t wave_max[Cfg<NMAX>::kWaves];
+  uint32_t wave_bound[Cfg<I>::kWaves];
+  uint32_t wave_max[Cfg<I>::kWaves];
   uint64_t prefix;
   uint32_t count;
   uint32_t gcount;
@@ -305,10 +328,10 @@ __device__ inline void next_digit(SM &sm, uint64_t prefix, int pbits, int krem, 
 // (take_all: the bound is key 0, which every element reaches; otherwise the test is
 // x >= bf in floats, see key_float), in raw form.  (Positions are 32-bit: a row
 // holds fewer than 2^31 elements.)
-template <int NMAX>
+template <int I>
 __device__ inline void append_piece(const float4 x, int32_t base, int32_t n, bool take_all, float bf,
-                                    Smem<NMAX> &sm, int lane) {
-  constexpr int kCandCap = Cfg<NMAX>::kCand;
+                                    Smem<I> &sm, int lane) {
+  constexpr int kCandCap = Cfg<I>::kCand;
   const float xs[4] = {x.x, x.y, x.z, x.w};
   // One ballot per element slot: the wave's selected elements of slot e go to
   // consecutive positions after those of slots 0 .. e-1 (the list's order is free).
@@ -340,8 +363,8 @@ __device__ inline void append_piece(const float4 x, int32_t base, int32_t n, boo
 // GMAX: the score kernel's per-row maxima of 16-pool groups are available (row pitch
 // ldg).  For long rows the bound then comes from the group maxima, and only the
 // groups whose max reaches it are read.
-template <bool GMAX, int NMAX>
-__global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
+template <bool GMAX, int I>
+__global__ __launch_bounds__(Cfg<I>::kThreads) void topk_kernel(const float *__restrict__ scores, int64_t ld,
                                                         const int32_t *__restrict__ n_valid,
                                                         const int32_t *__restrict__ cu_seqlens,
                                                         int nseq, int64_t grow0, int kpool,
@@ -349,14 +372,15 @@ __global__ __launch_bounds__(Cfg<NMAX>::kThreads) void topk_kernel(const float *
                                                         int32_t *__restrict__ out,
                                                         const float *__restrict__ gmax,
                                                         int64_t ldg) {
-  constexpr int kThreads = Cfg<NMAX>::kThreads;
-  constexpr int kWavesT = Cfg<NMAX>::kWaves;
-  constexpr int kRound = Cfg<NMAX>::kRound;
-  constexpr int kPieces = Cfg<NMAX>::kPieces;
-  constexpr int kCandCap = Cfg<NMAX>::kCand;
-  constexpr int kGroupCap = Cfg<NMAX>::kGroups;
+  constexpr int NMAX = Cfg<I>::kNmax;
+  constexpr int kThreads = Cfg<I>::kThreads;
+  constexpr int kWavesT = Cfg<I>::kWaves;
+  constexpr int kRound = Cfg<I>::kRound;
+  constexpr int kPieces = Cfg<I>::kPieces;
+  constexpr int kCandCap = Cfg<I>::kCand;
+  constexpr int kGroupCap = Cfg<I>::kGroups;
   static_assert(kRound % NMAX == 0, "group maxima per round");
-  __shared__ Smem<NMAX> sm;
+  __shared__ Smem<I> sm;
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -671,12 +695,12 @@ __global__ __launch_bounds__(256) void scores_copy_kernel(const float *__restric
 
 }  // namespace
 
-template <bool GMAX, int NMAX>
+template <bool GMAX, int I>
 static void launch_topk_inst(const float *scores, int64_t ld, int64_t nrows, const int32_t *n_valid,
                              const int32_t *cu_seqlens, int32_t nseq, int64_t grow0, int32_t kpool,
                              bool tail, int32_t budget, int32_t *out, const float *gmax, int64_t ldg,
                              hipStream_t stream) {
-  hipLaunchKernelGGL((topk_kernel<GMAX, NMAX>), dim3((unsigned)nrows), dim3(Cfg<NMAX>::kThreads), 0,
+  hipLaunchKernelGGL((topk_kernel<GMAX, I>), dim3((unsigned)nrows), dim3(Cfg<I>::kThreads), 0,
                      stream, scores, ld, n_valid, cu_seqlens, nseq, grow0, kpool, tail, budget, out,
                      gmax, ldg);
 }
@@ -687,22 +711,24 @@ hipError_t launch_topk(const float *scores, int64_t ld, int64_t nrows, const int
                        hipStream_t stream) {
   if (nrows <= 0) return hipSuccess;
   if (budget > kTopkMaxBudget) return hipErrorInvalidValue;
-  // budgets above 512 need more maxima per thread for a tight bound (and longer lists)
-  const bool big = budget > 512;
-  if (gmax && big)
-    launch_topk_inst<true, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
-                              budget,
-                              out, gmax, ldg, stream);
-  else if (gmax)
-    launch_topk_inst<true, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
-                              budget, out, gmax, ldg, stream);
-  else if (big)
-    launch_topk_inst<false, 8>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
-                              budget,
-                               out, gmax, ldg, stream);
-  else
-    launch_topk_inst<false, 4>(scores, ld, nrows, n_valid, cu_seqlens, nseq, grow0, kpool, tail,
-                              budget, out, gmax, ldg, stream);
+  // larger budgets need more maxima per row for a tight bound, and longer lists
+  const int inst = budget <= Cfg<0>::kMaxBudget ? 0 : budget <= Cfg<1>::kMaxBudget ? 1 : 2;
+  auto go = [&](auto gm, auto ic) {
+    launch_topk_inst<decltype(gm)::value, decltype(ic)::value>(scores, ld, nrows, n_valid, cu_seqlens,
+                                                               nseq, grow0, kpool, tail, budget, out,
+                                                               gmax, ldg, stream);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (gmax) {
+    if (inst == 0) go(T_{}, std::integral_constant<int, 0>{});
+    else if (inst == 1) go(T_{}, std::integral_constant<int, 1>{});
+    else go(T_{}, std::integral_constant<int, 2>{});
+  } else {
+    if (inst == 0) go(F_{}, std::integral_constant<int, 0>{});
+    else if (inst == 1) go(F_{}, std::integral_constant<int, 1>{});
+    else go(F_{}, std::integral_constant<int, 2>{});
+  }
   return hipGetLastError();
 }
 
