@@ -298,14 +298,16 @@ class Selector:
 
     Holds the device copies of cu_seqlens / cu_pools and a workspace sized
     for the row range; `run` enqueues the three library calls on one stream.
-    overlap=True (the default) sizes the workspace for two chunk buffers and runs
-    the chunk loop with KPOOL_FLAG_OVERLAP; workspace_cap caps the workspace
-    (smaller chunks); tail=True runs every step in tail mode (KPOOL_FLAG_TAIL).
+    By default the workspace is one chunk buffer, so all fp32 scores in flight stay
+    within the 2 GiB cap; overlap=True sizes it for two chunk buffers and runs the
+    chunk loop with KPOOL_FLAG_OVERLAP (two chunks in flight on two streams);
+    workspace_cap caps the workspace (smaller chunks); tail=True runs every step in
+    tail mode (KPOOL_FLAG_TAIL).
     """
 
     def __init__(self, cu_seqlens, kpool: int, budget: int, H: int, D: int, device="cuda",
                  q_lo: int = 0, q_hi: int | None = None, workspace_cap: int | None = None,
-                 scale: float | None = None, overlap: bool = True, tail: bool = False):
+                 scale: float | None = None, overlap: bool = False, tail: bool = False):
         import torch
         self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
         self.T = int(self.cu[-1])
