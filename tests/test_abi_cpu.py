@@ -179,3 +179,59 @@ def test_gated_pool_keys_rejects_bad_arguments():
     cu0 = np.array([0, 0], dtype=np.int32)
     assert L.kpool_pool_keys_gated(None, None, None, cu0.ctypes.data_as(vp), None, None, 1, 16, 4, 0,
                                    None, None) == K.KPOOL_OK
+
+
+C_USER = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "kpool.h"
+
+/* the call sequence of one pass, as a C caller writes it (type-checked, not run) */
+int one_pass(const uint16_t *q, const uint16_t *k, const float *w, const int32_t *cu_host,
+             const int32_t *cu_dev, const int32_t *cu_pools_dev, int32_t nseq, int64_t T,
+             uint16_t *kp, void *workspace, int32_t *pool_ids, float *scores, int32_t *token_ids,
+             void *stream) {
+  int32_t cu_pools_host[64];
+  int32_t max_pools = 0;
+  int32_t nbuf = 0;
+  int64_t P = kpool_count_pools(cu_host, nseq, 4, 0, cu_pools_host, &max_pools);
+  if (P < 0) return (int)P;
+  int rc = kpool_pool_keys(k, cu_host, cu_dev, cu_pools_dev, nseq, 128, 4, 0, kp, stream);
+  if (rc != KPOOL_OK) { fprintf(stderr, "%s\n", kpool_last_error()); return rc; }
+  size_t ws = kpool_workspace_bytes(0, T, max_pools, 1);
+  int64_t rows = kpool_chunk_rows(max_pools, ws, 0, &nbuf);
+  (void)rows;
+  rc = kpool_score_topk(q, kp, w, cu_host, cu_dev, nseq, 32, 128, 4, 0.08838835f, 0, T, 512,
+                        workspace, ws, 0, pool_ids, scores, stream);
+  if (rc != KPOOL_OK) return rc;
+  rc = kpool_score_topk_noalloc(q, kp, w, cu_host, cu_dev, nseq, 32, 128, 4, 0.08838835f, 0, T,
+                                512, KPOOL_FLAG_TAIL, pool_ids, NULL, stream);
+  if (rc != KPOOL_OK) return rc;
+  rc = kpool_expand(pool_ids, cu_host, cu_dev, nseq, 4, 0, T, 512, 0, token_ids, stream);
+  if (rc != KPOOL_OK) return rc;
+  rc = kpool_pool_keys_gated(k, k, w, cu_host, cu_dev, cu_pools_dev, nseq, 128, 4,
+                             KPOOL_FLAG_TAIL, kp, stream);
+  if (rc != KPOOL_OK) return rc;
+  rc = kpool_topk(scores, 64, cu_dev, T, 512, pool_ids, stream);
+  double ms[KPOOL_PROFILE_KINDS];
+  int64_t launches[KPOOL_PROFILE_KINDS];
+  kpool_profile_enable(1);
+  kpool_profile_collect(ms, launches);
+  return rc + kpool_version() * 0 + (int)KPOOL_NOALLOC_SCRATCH_BYTES * 0 + (int)KPOOL_FLAG_OVERLAP * 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_the_call_sequence_type_checks(tmp_path):
+    """include/kpool.h is a C header (the boundary is a C ABI): a C99 caller that makes
+    every call compiles with warnings as errors (syntax and types only; nothing is run)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "user.c"
+    src.write_text(C_USER)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-I", os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
