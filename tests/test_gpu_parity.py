@@ -197,23 +197,26 @@ def test_row_split_and_chunking_reassemble_bitwise(kpool, budget):
         np.testing.assert_array_equal(serial[key], full[key], err_msg=key)
 
 
-def test_per_token_long_rows_use_group_pruning():
-    """kpool 1, budget 2048, rows that see more than 65536 pools: the top-k reads the
-    score kernel's group maxima first (8 per thread) and then only candidate groups;
-    checked against the oracle on a window of such rows, with a small workspace so the
-    window spans several chunks."""
+@pytest.mark.parametrize("budget", [2048, 1000, 600, 512])
+def test_per_token_long_rows_use_group_pruning(budget):
+    """kpool 1, rows that see more than 65536 pools (4100+ groups of 16): the top-k reads
+    the score kernel's group maxima first and then only candidate groups, in each of its
+    instances (budget 2048: 8 maxima per thread over 512 threads; 1000 and 600: 4 over
+    512; 512: 4 over 256); checked against the oracle on a window of such rows, with a
+    small workspace so the window spans several chunks."""
     wl, r = _inputs("sq4096_k1", 11, T=67000)
     lo, hi = 66000, 66090
     pitch = (67000 + 63) // 64 * 64
-    res = run_gpu(r, 1, 2048, q_lo=lo, q_hi=hi, workspace_cap=20 * (pitch + pitch // 16) * 4)
+    res = run_gpu(r, 1, budget, q_lo=lo, q_hi=hi, workspace_cap=20 * (pitch + pitch // 16) * 4)
     rows = np.arange(lo, hi)
     kp, o_scores, t = oracle_rows(r, 1, rows, width=res["max_pools"])
     np.testing.assert_array_equal(res["kp"], kp)
     nvis = t + 1
-    check_scores(res["scores"], o_scores, nvis, "k1 long")
-    check_topk_self(res["scores"], res["pool_ids"], nvis, 2048, "k1 long")
-    check_selection_vs_oracle(res["pool_ids"], o_scores, nvis, 2048, "k1 long")
-    check_tokens(res["token_ids"], res["pool_ids"], t, 1, where="k1 long")
+    where = f"k1 long budget {budget}"
+    check_scores(res["scores"], o_scores, nvis, where)
+    check_topk_self(res["scores"], res["pool_ids"], nvis, budget, where)
+    check_selection_vs_oracle(res["pool_ids"], o_scores, nvis, budget, where)
+    check_tokens(res["token_ids"], res["pool_ids"], t, 1, where=where)
 
 
 def test_thd_packing_invariance():
