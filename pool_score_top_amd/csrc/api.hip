@@ -321,6 +321,11 @@ int score_topk_impl(const char *fn, const uint16_t *q, const uint16_t *kp, const
         max_npv = std::max<int32_t>(max_npv, std::min((sg.hi - 1 - sg.start) / kpool + 1, sg.pool_count));
       }
       L.tile_start[L.nseg] = ntiles;
+      // No row of these sequences sees a pool (tail mode: each is shorter than kpool), so
+      // there is nothing to score; the selection writes their ids as -1 without reading
+      // scores, and the scores_out copy writes -inf.  (A zero-segment launch would have
+      // an empty grid.)
+      if (max_npv == 0) continue;
       // Pool segments per tile: at most KPOOL_SCORE_TARGET_WGS workgroups per launch (4 per
       // CU), segments of 64..kPoolSegMax pools; fewer, longer workgroups reload q less
       // often.  Among the segment counts from that target down to the fewest the size cap

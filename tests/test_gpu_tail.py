@@ -95,6 +95,22 @@ def test_tail_mode_indexer_shape(kpool, budget):
     _check_all(r, cu, kpool, budget, res, f"tail 3001 kpool {kpool}")
 
 
+@pytest.mark.parametrize("overlap", [False, True])
+def test_tail_mode_one_row_chunks_over_sequences_without_pools(overlap):
+    """One-row chunks (a one-row workspace) in tail mode, over a batch in which sequences
+    shorter than kpool (no full pool, so no visible pool for any of their rows) sit
+    between sequences with pools: a chunk that holds only such a row has nothing to
+    score, and its rows must still come out as -1 ids and tail tokens."""
+    cu = np.array([0, 1, 12, 14, 25, 26, 40, 43, 60], dtype=np.int32)
+    kpool, budget = 4, 8
+    wl = synth.workload("tiny", T=60)
+    r = synth.host_inputs(wl, 70)
+    _, max_pools, _ = K.count_pools(cu, kpool, tail=True)
+    cap = K.workspace_bytes(0, 1, max_pools, 1)
+    res = _run(r, cu, kpool, budget, workspace_cap=cap, overlap=overlap)
+    _check_all(r, cu, kpool, budget, res, f"tail one-row chunks overlap={overlap}")
+
+
 def test_tail_mode_gated_pooling():
     cu = np.array([0, 7, 7, 50, 99, 100], dtype=np.int32)
     wl = synth.workload("tiny_gated", T=100)
