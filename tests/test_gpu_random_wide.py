@@ -5,7 +5,9 @@ selection reads group maxima and prunes), checked on a window of up to 200 rows 
 the oracle scores on its own; kpool 1..16; any budget 1..2048 (every selection
 instance); batches of up to 70 sequences (the score launch splits its segment list);
 workspaces of 1, 2, 7 or 100 rows or the default, with or without the chunk overlap;
-and the allocation-free entry point.  The rules are those of the other parity tests.
+the allocation-free entry point; a score scale from 0.01 to 10 (the ABI takes any scale
+> 0); and inputs with signed head weights, exact score ties (keys from {-1, 0, 1}),
+all-zero weights or constant keys (every score tied: the selection's exact path).  The rules are those of the other parity tests.
 Megatron-LM PR #8299, "Test plan" and "Change".
 """
 import numpy as np
@@ -45,8 +47,10 @@ def _config(case):
     ws_rows = [None, 1, 2, 7, 100][int(rng.integers(0, 5))]
     overlap = bool(rng.integers(0, 2))
     noalloc = bool(rng.integers(0, 4) == 0)
+    scale = float(np.float32(10.0 ** rng.uniform(-2, 1)))
+    variant = str(rng.choice(["", "", "w_neg", "k_ternary", "w_zero", "k_const"]))
     return dict(kpool=kpool, T=T, cu=cu, budget=budget, tail=tail, gated=gated, q_lo=q_lo, q_hi=q_hi,
-                ws_rows=ws_rows, overlap=overlap, noalloc=noalloc)
+                ws_rows=ws_rows, overlap=overlap, noalloc=noalloc, scale=scale, variant=variant)
 
 
 @pytest.mark.parametrize("case", range(NCASES))
@@ -55,7 +59,8 @@ def test_wide_random_configuration(case):
     kpool, T, cu, budget, tail = c["kpool"], c["T"], c["cu"], c["budget"], c["tail"]
     where = f"wide case {case}: " + str({k: v for k, v in c.items() if k != 'cu'}) + f" nseq={len(cu) - 1}"
     print(f"[case] {where}", flush=True)
-    wl = synth.workload("sq4096_gated" if c["gated"] else "sq4096", T=T, kpool=kpool, budget=budget)
+    wl = synth.workload("sq4096_gated" if c["gated"] else "sq4096", T=T, kpool=kpool, budget=budget,
+                        variant=c["variant"])
     r = synth.host_inputs(wl, 5000 + case)
     cu_pools_h, max_pools, P = K.count_pools(cu, kpool, tail=tail)
     q, k, w = device_tensors(r)
@@ -72,7 +77,8 @@ def test_wide_random_configuration(case):
     scores = torch.empty((n, max(max_pools, 1)), dtype=torch.float32, device="cuda")
     so = scores if max_pools else None
     if c["noalloc"]:
-        K.score_topk_noalloc(q, kp, w, cu, cu_dev, kpool, budget, c["q_lo"], c["q_hi"], ids, scores_out=so, tail=tail)
+        K.score_topk_noalloc(q, kp, w, cu, cu_dev, kpool, budget, c["q_lo"], c["q_hi"], ids, scores_out=so,
+                             scale=c["scale"], tail=tail)
     else:
         ws = None
         if max_pools:
@@ -80,8 +86,8 @@ def test_wide_random_configuration(case):
             if c["ws_rows"] is not None:
                 nb = min(nb, K.workspace_bytes(0, c["ws_rows"], max_pools, 1))
             ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
-        K.score_topk(q, kp, w, cu, cu_dev, kpool, budget, c["q_lo"], c["q_hi"], workspace=ws, pool_ids=ids,
-                     scores_out=so, overlap=c["overlap"], tail=tail)
+        K.score_topk(q, kp, w, cu, cu_dev, kpool, budget, c["q_lo"], c["q_hi"], scale=c["scale"], workspace=ws,
+                     pool_ids=ids, scores_out=so, overlap=c["overlap"], tail=tail)
     tok = K.expand(ids, cu, cu_dev, kpool, budget, c["q_lo"], c["q_hi"], tail=tail)
     torch.cuda.synchronize()
     g_kp = kp.cpu().numpy().view(np.uint16)[:P]
@@ -92,7 +98,8 @@ def test_wide_random_configuration(case):
     else:
         kp_o = oracle.pool_keys(r["k"], cu, kpool, tail=tail)
     assert np.array_equal(g_kp, kp_o), where + ": kp"
-    ref = oracle.select(r["q"], r["k"], r["w"], cu, kpool, budget, q_lo=c["q_lo"], q_hi=c["q_hi"], kp_bits=kp_o, tail=tail)
+    ref = oracle.select(r["q"], r["k"], r["w"], cu, kpool, budget, q_lo=c["q_lo"], q_hi=c["q_hi"],
+                        scale=c["scale"], kp_bits=kp_o, tail=tail)
     rows = np.arange(c["q_lo"], c["q_hi"])
     cu_pools, _ = oracle.count_pools(cu, kpool, tail=tail)
     seq, t = oracle.row_positions(rows, cu)
