@@ -7,8 +7,10 @@ instance); batches of up to 70 sequences (the score launch splits its segment li
 workspaces of 1, 2, 7 or 100 rows or the default, with or without the chunk overlap;
 the allocation-free entry point; a score scale from 0.01 to 10 (the ABI takes any scale
 > 0); and inputs with signed head weights, exact score ties (keys from {-1, 0, 1}),
-all-zero weights or constant keys (every score tied: the selection's exact path).  The rules are those of the other parity tests.
-Megatron-LM PR #8299, "Test plan" and "Change".
+all-zero weights or constant keys (every score tied: the selection's exact path).  The
+family runs on both compiled score shapes: H=32, D=128 (24 cases, windows of up to 200
+rows) and H=4, D=16 (32 cases, windows of up to 600 rows).  The rules are those of the
+other parity tests.  Megatron-LM PR #8299, "Test plan" and "Change".
 """
 import numpy as np
 import pytest
@@ -21,11 +23,16 @@ from pool_score_top_amd import kpool as K
 from pool_score_top_amd import synth
 
 pytestmark = pytest.mark.gpu
-NCASES = 24
+# shape: (workload, gated workload, case seed base, input seed base, window rows, cases)
+SHAPES = {
+    "h32d128": ("sq4096", "sq4096_gated", 90000, 5000, 200, 24),
+    "h4d16": ("tiny", "tiny_gated", 120000, 8000, 600, 32),
+}
+CASES = [(shape, case) for shape, v in SHAPES.items() for case in range(v[5])]
 
 
-def _config(case):
-    rng = np.random.default_rng(90000 + case)
+def _config(case, seed_base, window):
+    rng = np.random.default_rng(seed_base + case)
     kpool = int(rng.integers(1, 17))
     big = rng.integers(0, 3) == 0
     T = int(rng.integers(16384, 70001)) if big else int(rng.integers(1, 6001))
@@ -38,7 +45,7 @@ def _config(case):
     gated = bool(rng.integers(0, 5) == 0)
     if big:
         q_lo = int(rng.integers(0, T))
-        q_hi = min(T, q_lo + int(rng.integers(1, 200)))
+        q_hi = min(T, q_lo + int(rng.integers(1, window)))
     else:
         q_lo, q_hi = 0, T
         if rng.integers(0, 2):
@@ -53,15 +60,17 @@ def _config(case):
                 ws_rows=ws_rows, overlap=overlap, noalloc=noalloc, scale=scale, variant=variant)
 
 
-@pytest.mark.parametrize("case", range(NCASES))
-def test_wide_random_configuration(case):
-    c = _config(case)
+@pytest.mark.parametrize("shape,case", CASES)
+def test_wide_random_configuration(shape, case):
+    wl_name, wl_gated, seed_base, input_seed, window, _ = SHAPES[shape]
+    c = _config(case, seed_base, window)
     kpool, T, cu, budget, tail = c["kpool"], c["T"], c["cu"], c["budget"], c["tail"]
-    where = f"wide case {case}: " + str({k: v for k, v in c.items() if k != 'cu'}) + f" nseq={len(cu) - 1}"
+    where = (f"wide case {shape}/{case}: " + str({k: v for k, v in c.items() if k != 'cu'}) +
+             f" nseq={len(cu) - 1}")
     print(f"[case] {where}", flush=True)
-    wl = synth.workload("sq4096_gated" if c["gated"] else "sq4096", T=T, kpool=kpool, budget=budget,
+    wl = synth.workload(wl_gated if c["gated"] else wl_name, T=T, kpool=kpool, budget=budget,
                         variant=c["variant"])
-    r = synth.host_inputs(wl, 5000 + case)
+    r = synth.host_inputs(wl, input_seed + case)
     cu_pools_h, max_pools, P = K.count_pools(cu, kpool, tail=tail)
     q, k, w = device_tensors(r)
     n = c["q_hi"] - c["q_lo"]
