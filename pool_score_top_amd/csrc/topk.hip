@@ -115,25 +115,23 @@ __device__ inline float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// The rank-th largest (1-based, duplicates counted) of the wave's 64*NMAX values,
-// by a radix descent over the 32 bits: at each bit, the values that match the bits
-// decided so far and have this bit set are counted with ballots; if there are at
-// least `rank` of them the answer has the bit set, otherwise it has the bit clear
-// and those values are skipped.  The result is wave-uniform.
+// The rank-th largest (1-based, duplicates counted) of the wave's 64*NMAX values: the
+// largest t with at least `rank` values >= t, found by a binary search over t's bits
+// from the top (t = the bits decided so far with this bit set; keep the bit if enough
+// values reach t).  One compare per value and bit, against a wave-uniform threshold;
+// the counts are ballots.  The result is wave-uniform.
 template <int NMAX>
 __device__ inline uint32_t wave_kth_desc(const uint32_t (&x)[NMAX], int rank) {
-  uint32_t prefix = 0;
-  int r = rank;
+  uint32_t v = 0;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
-    const uint32_t want = (prefix >> b) | 1u;  // decided bits above b, then bit b set
+    const uint32_t t = v | (1u << b);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) cnt += __popcll(__ballot((x[i] >> b) == want));
-    if (cnt >= r) prefix |= 1u << b;
-    else r -= cnt;
+    for (int i = 0; i < NMAX; ++i) cnt += __popcll(__ballot(x[i] >= t));
+    if (cnt >= rank) v = t;
   }
-  return prefix;
+  return v;
 }
 
 // The value of lane (lane ^ D), D a power of two below 64, with D known at compile
