@@ -233,8 +233,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--workspace-mib", type=int, default=None,
-                    help="cap the score workspace (default: two full 2 GiB chunk buffers); "
-                         "smaller workspaces mean shorter chunks")
+                    help="cap the score workspace (default: one 2 GiB chunk buffer, two with "
+                         "--overlap on); smaller workspaces mean shorter chunks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (scales the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")

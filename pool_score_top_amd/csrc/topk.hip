@@ -237,6 +237,8 @@ __device__ void sort_and_write(uint64_t *cand, uint32_t count, int budget, int32
     const int i = tid * M + m;
     if (i < budget) orow[i] = (v[m] != 0ull) ? (int32_t)(~(uint32_t)v[m]) : -1;
   }
+  // output slots past the sort size: the row has fewer candidates than that
+  for (int i = M * kThreads + tid; i < budget; i += kThreads) orow[i] = -1;
 }
 
 template <int I>
@@ -667,12 +669,11 @@ __global__ __launch_bounds__(Cfg<I>::kThreads) void topk_kernel(const float *__r
     count = (uint32_t)budget;
   }
 
-  // The sort must also cover every output slot (missing ones are written as -1).  Its
-  // span is at most 4 kThreads: a list in a larger sort class than the budget was cut
-  // to the budget above, and budgets are at most 4 kThreads.
-  const uint32_t span = max(count, (uint32_t)budget);
-  if (span <= (uint32_t)kThreads) sort_and_write<1, kThreads>(list, count, budget, orow, tid);
-  else if (span <= 2u * kThreads) sort_and_write<2, kThreads>(list, count, budget, orow, tid);
+  // The sort covers the list in the smallest sort size that holds it (at most 4 kThreads
+  // keys: a list in a larger sort class than the budget was cut to the budget above, and
+  // budgets are at most 4 kThreads); a short row's slots past it are written as -1.
+  if (count <= (uint32_t)kThreads) sort_and_write<1, kThreads>(list, count, budget, orow, tid);
+  else if (count <= 2u * kThreads) sort_and_write<2, kThreads>(list, count, budget, orow, tid);
   else sort_and_write<4, kThreads>(list, count, budget, orow, tid);
 }
 

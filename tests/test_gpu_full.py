@@ -1,8 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times.
 
 The whole selection runs over 262144 and 524288 tokens (and the heaviest 1/8
-query slice of 524288), with the workspace bench.py uses (two 2 GiB chunk
-buffers, chunks alternating between two streams).  Then, for at least 16
+query slice of 524288), with the workspace bench.py uses (one 2 GiB chunk
+buffer, chunks one after the other on one stream).  Then, for at least 16
 windows of 64 consecutive rows per workload (the first rows, both sides of
 several chunk edges, the last rows, and seeded random windows):
 
