@@ -253,6 +253,30 @@ def test_weight_doubling_doubles_scores_exactly():
     np.testing.assert_array_equal(b["pool_ids"], a["pool_ids"])
 
 
+def test_head_permutation_changes_scores_only_by_rounding():
+    # Permuting the heads of q and w together leaves the formula unchanged; on the GPU it
+    # only reorders the fp32 head sum.  Both runs must pass every oracle rule, and their
+    # scores differ by at most a few fp32 roundings of the head sum.
+    wl, r = _inputs("sq4096", 11, T=1500, budget=200)
+    a = run_gpu(r, wl.kpool, wl.budget)
+    perm = np.random.default_rng(5).permutation(wl.H)
+    assert (perm != np.arange(wl.H)).any()
+    r2 = dict(r)
+    r2["q"] = np.ascontiguousarray(r["q"][:, perm, :])
+    r2["w"] = np.ascontiguousarray(r["w"][:, perm])
+    b = run_gpu(r2, wl.kpool, wl.budget)
+    for res, where in ((a, "heads in order"), (b, "heads permuted")):
+        _full_check(wl, r, res, where=where)
+    vis = np.isfinite(a["scores"])
+    np.testing.assert_array_equal(vis, np.isfinite(b["scores"]))
+    # (w >= 0 here, so the head sum has no cancellation: each ordering is within
+    # H * 2^-24 of the exact sum, relative)
+    av, bv = a["scores"][vis], b["scores"][vis]
+    diff = np.abs(av - bv)
+    assert (diff <= 2 * wl.H * 2.0 ** -24 * np.abs(av)).all(), diff.max()
+    print(f"[heads] permuted heads: max score change {diff.max():.2e}", flush=True)
+
+
 def test_zero_weights_select_by_index():
     wl, r = _inputs("sq4096", 0, T=3000, variant="w_zero")
     res = run_gpu(r, wl.kpool, wl.budget)
