@@ -62,7 +62,24 @@ def build(verbose: bool = False, extra=()) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for _, o in jobs]], verbose)
     os.replace(tmp, LIB)
+    build_example(verbose)
     return LIB
+
+
+EXAMPLE_SRC = os.path.join(HERE, "examples", "select_file.c")
+EXAMPLE = os.path.join(HERE, "examples", "select_file")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_example(verbose: bool = False) -> str:
+    """The C example (a plain C99 host program over the C ABI and the HIP runtime),
+    built with the system C compiler against the library next to it."""
+    tmp = EXAMPLE + ".tmp"
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          f"-I{ROCM}/include", EXAMPLE_SRC, "-o", tmp, f"-L{HERE}", "-lkpool", f"-L{ROCM}/lib",
+          "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/..", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    os.replace(tmp, EXAMPLE)
+    return EXAMPLE
 
 
 if __name__ == "__main__":

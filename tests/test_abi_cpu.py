@@ -235,3 +235,18 @@ def test_header_is_plain_c_and_the_call_sequence_type_checks(tmp_path):
     r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
                         "-I", os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_c_example_is_built_and_rejects_bad_usage(tmp_path):
+    # the C example over the ABI (examples/select_file.c); these paths return before any
+    # HIP call, so they run without a GPU
+    import subprocess
+    from pool_score_top_amd import build as B
+    assert os.path.exists(B.EXAMPLE), "the C example is not built; run __graft_entry__.build()"
+    p = subprocess.run([B.EXAMPLE], capture_output=True, text=True, timeout=60)
+    assert p.returncode == 2 and "usage" in p.stderr
+    short = tmp_path / "short.bin"
+    np.array([64, 4, 16, 4, 4, 1, 0, 64], dtype="<i4").tofile(short)  # header and cu_seqlens only
+    p = subprocess.run([B.EXAMPLE, str(short), str(tmp_path / "out.bin")], capture_output=True, text=True,
+                       timeout=60)
+    assert p.returncode == 2 and "short input" in p.stderr
