@@ -385,6 +385,20 @@ __global__ __launch_bounds__(Cfg<I>::kThreads) void topk_kernel(const float *__r
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const float *row = scores + r * ld;
+  const float *grow = GMAX ? gmax + r * ldg : nullptr;
+  // Pass 1's first round of group maxima is requested before the row's length is known
+  // (its lookup below is a dependent load, and a launch's rows all start at once):
+  // indices are clamped to the row pitch, so the loads stay in the buffer, and those
+  // past the row's groups are masked in pass 1.  Only when the pitch admits the group
+  // path, which needs at least NMAX*kThreads groups, so that short rows do not pay.
+  // (1.1% of the selection time at kpool 1, 0.3% at 512k tokens.)
+  const bool early = GMAX && ldg >= (int64_t)NMAX * kThreads;
+  float v0[kRound];
+  if (early) {
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) v0[j] = grow[min<int64_t>(tid + j * kThreads, ldg - 1)];
+  }
   int64_t n;
   if (n_valid) {
     n = min<int64_t>(max<int64_t>(n_valid[r], 0), ld);
@@ -393,17 +407,28 @@ __global__ __launch_bounds__(Cfg<I>::kThreads) void topk_kernel(const float *__r
     const int s = find_seq(cu_seqlens, nseq, i);
     n = visible_count(i - cu_seqlens[s], cu_seqlens[s + 1] - cu_seqlens[s], kpool, tail);
   }
-  const float *row = scores + r * ld;
-  const float *grow = GMAX ? gmax + r * ldg : nullptr;
   const int64_t ng = (n + kGroup - 1) / kGroup;  // 16-pool groups of the row
   // Group maxima are used when each of a thread's NMAX maxima covers at least one of
   // them (so every wave contributes 64*NMAX real maxima); shorter rows are read in full.
+  // (n <= ld, so ng <= ldg: the group path implies `early`.)
   const bool use_groups = GMAX && n > budget && ng >= (int64_t)NMAX * kThreads;
   int32_t *orow = out + r * (int64_t)budget;
   if (tid == 0) {
     sm.count = 0;
     sm.gcount = 0;
     sm.scount = 0;
+  }
+
+  // A row with at most `budget` visible pools keeps all of them: their keys go straight
+  // into the list (element i in slot i) and are sorted; there is nothing to bound or cut.
+  if (n <= budget) {
+    const int32_t n32 = (int32_t)n;  // <= budget <= 4 kThreads <= the list's capacity
+    for (int32_t i = tid; i < n32; i += kThreads) sm.cand[i] = compose(order_key(row[i]), (uint32_t)i);
+    __syncthreads();
+    if (n32 <= kThreads) sort_and_write<1, kThreads>(sm.cand, (uint32_t)n32, budget, orow, tid);
+    else if (n32 <= 2 * kThreads) sort_and_write<2, kThreads>(sm.cand, (uint32_t)n32, budget, orow, tid);
+    else sort_and_write<4, kThreads>(sm.cand, (uint32_t)n32, budget, orow, tid);
+    return;  // (n is the same for the whole workgroup)
   }
 
   // ---- pass 1: lower bound on the budget-th best key ----------------------
@@ -419,8 +444,12 @@ __global__ __launch_bounds__(Cfg<I>::kThreads) void topk_kernel(const float *__r
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) fmx[i] = __uint_as_float(0x7FC00000u);
     if (use_groups) {
-      // rounds of kRound independent loads per thread; item j goes to maximum j % NMAX
-      for (int64_t gb = 0; gb < ng; gb += (int64_t)kThreads * kRound) {
+      // rounds of kRound independent loads per thread; item j goes to maximum j % NMAX;
+      // round 0 was loaded early
+#pragma unroll
+      for (int j = 0; j < kRound; ++j)
+        if (tid + j * kThreads < ng) fmx[j % NMAX] = fmaxf(fmx[j % NMAX], v0[j]);
+      for (int64_t gb = (int64_t)kThreads * kRound; gb < ng; gb += (int64_t)kThreads * kRound) {
         float v[kRound];
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
