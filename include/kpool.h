@@ -231,7 +231,8 @@ int kpool_expand(const int32_t *pool_ids, const int32_t *cu_seqlens_host,
  * half of the chunk loop, exposed so it can be checked on its own).
  *   scores   fp32 [rows, ld], ld % 4 == 0, 16-byte aligned
  *   n_valid  int32 [rows] device: row r ranks scores[r, 0 .. n_valid[r]),
- *            0 <= n_valid[r] <= ld
+ *            0 <= n_valid[r] <= ld (a value outside is clamped to that range: a
+ *            negative count selects nothing, one past ld ranks the whole row)
  *   budget   1..2048, as for kpool_score_topk
  *   pool_ids int32 [rows, budget]: same ordering and padding as kpool_score_topk */
 int kpool_topk(const float *scores, int64_t ld, const int32_t *n_valid, int64_t rows,

@@ -336,6 +336,19 @@ def test_topk_standalone_matches_oracle_selection(budget):
         assert np.array_equal(got[i], want), f"row {i} (n={len(x)})"
 
 
+def test_topk_standalone_clamps_row_counts():
+    # counts outside [0, ld] are clamped: negative -> nothing selected, beyond ld -> the row
+    rng = np.random.default_rng(17)
+    ld = 5000
+    buf = rng.standard_normal((4, ld)).astype(np.float32)
+    for budget in (7, 600, 2048):
+        nv = np.array([-5, ld + 1000, 0, ld], dtype=np.int32)
+        got = K.topk(torch.from_numpy(buf).cuda(), torch.from_numpy(nv).cuda(), budget).cpu().numpy()
+        assert np.all(got[0] == -1) and np.all(got[2] == -1), budget
+        for i in (1, 3):
+            assert np.array_equal(got[i], oracle.select_row_full_sort(buf[i], budget)), (budget, i)
+
+
 def test_expand_standalone_matches_oracle():
     rng = np.random.default_rng(3)
     for kpool in (1, 3, 4):
