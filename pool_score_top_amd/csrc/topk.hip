@@ -14,11 +14,12 @@
 //
 //   pass 1  (HBM)   every thread keeps NMAX maxima over disjoint parts of its
 //                   elements (or, for long rows, of its 16-pool group maxima,
-//                   written by the score kernel).  In each wave the
-//                   ceil(budget/waves)-th largest of its 64*NMAX maxima is found
-//                   by a radix descent with ballots; the minimum L over the waves
-//                   is a lower bound on the budget-th best key (at least budget
-//                   distinct elements reach it).
+//                   written by the score kernel; the first round of those is
+//                   requested before the row's length is known).  In each wave
+//                   the ceil(budget/waves)-th largest of its 64*NMAX maxima is
+//                   found by a binary search on a ballot count; the minimum L
+//                   over the waves is a lower bound on the budget-th best key (at
+//                   least budget distinct elements reach it).
 //   pass 2  (L2)    elements with key >= L (for long rows: only inside the
 //                   groups whose max reaches L) are appended to an LDS candidate
 //                   list with one atomic per wave per step.  For iid scores the
@@ -35,8 +36,8 @@
 //                   over the 64-bit keys (8-bit digits, re-reading the row)
 //                   finds the budget-th key and collects exactly budget
 //                   elements, which are then sorted the same way.
-// Rows with no more than `budget` elements skip the bound and keep them all;
-// unused output slots are -1.
+// Rows with no more than `budget` elements keep them all: their keys go straight into
+// the list and are sorted, with no bound, append or cut.  Unused output slots are -1.
 #include <type_traits>
 
 #include "kpool_internal.h"
@@ -55,7 +56,7 @@ constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // order_key(-inf)
 // waves (iid rows of 16k-131k pools at budget 512: about 775 candidates in about 740
 // groups, at most 930 and 880 over 200 rows).  The top-k is latency-bound, so the
 // instances are sized for rows in flight: the small one's lists (16.4 KB of LDS) and
-// rounds of 8 group maxima or 4 score pieces per thread (52 VGPRs) let eight rows
+// rounds of 8 group maxima or 4 score pieces per thread (54 VGPRs) let eight rows
 // share a CU, the limit of eight waves per SIMD; the medium one's (31 KB) four rows of
 // 8 waves; the large one's (49 KB) three.  (Before the medium instance, budgets
 // 513-1024 ran on the large one: 27.3 vs 19.3 ms of top-k per 512k step at budget
